@@ -1,0 +1,599 @@
+/*
+ * fpo.c -- the oracle: a plain, slow, fp64 CPU statement of what the
+ * FlashPrefill V2 block-sparse prefill path computes.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or constant with the HIP path and must never be used to
+ * produce a product result.
+ *
+ * Sources (cited by page title and section/equation):
+ *   [V2]  "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context
+ *         LLM Serving" (arXiv 2608.19758).
+ *   [V1]  "FlashPrefill: Instantaneous Pattern Discovery and Thresholding for
+ *         Ultra-Fast Long-Context Prefilling" (summary page), sections 3.1-3.4.
+ *   [OCP] OCP 8-bit floating point specification, E4M3 ("FN") encoding.
+ *
+ * Everything is computed in double precision, one row / one block at a time,
+ * in the order the pages state it.  Readings taken where the pages leave a
+ * step open are marked READING and listed in the design notes.
+ *
+ * Conventions shared with every caller (they are definitions of the problem,
+ * not of the GPU path):
+ *   - q is [total, hq, d], k and v are [total, hkv, d], ragged by cu[] rows
+ *     (contiguous; paged inputs are de-paged by the caller with [V2] Eq. 22).
+ *   - packed row r of KV head h maps to position floor(r/g) and query head
+ *     h*g + (r mod g)                                     ([V2] §3.3 Eq. 12-13)
+ *   - a query tile is R consecutive packed rows of one (request, KV head);
+ *     segments are ordered (request, KV head, tile).      ([V2] §3.3 Eq. 17)
+ *   - blocks are B tokens, physical tiles are P tokens.   ([V2] §3.3 impl. details)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { FPO_F32 = 0, FPO_BF16 = 1, FPO_E4M3 = 2 };
+
+typedef struct {
+  int32_t num_reqs, hq, hkv, d;
+  const int64_t* cu;  /* [num_reqs+1] row offsets into q/k/v */
+  int32_t dtype;      /* FPO_* */
+  double cq, ck, cv;  /* per-tensor descales for E4M3 ([V2] §3.3 Eq. 15); 1 otherwise */
+  const void* q;
+  const void* k;
+  const void* v;
+  double scale;       /* softmax scale sigma = 1/sqrt(d) */
+  int32_t block;      /* B, selection block size */
+  int32_t rows;       /* R, packed rows per query tile */
+  int32_t phys;       /* P, physical key tile */
+} fpo_problem;
+
+/* ------------------------------------------------------------------ */
+/* element decoding                                                     */
+/* ------------------------------------------------------------------ */
+
+/* [OCP] E4M3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent
+ * field 0 is subnormal (2^-6 * m/8); S.1111.111 is NaN; there is no infinity.
+ * The largest finite value is 2^8 * 1.75 = 448. */
+double fpo_e4m3_decode(uint8_t x) {
+  int sign = (x >> 7) & 1;
+  int e = (x >> 3) & 15;
+  int m = x & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* Round-to-nearest-even into E4M3 by exhaustive search over the finite codes,
+ * saturating at +-448.  Only used by the optional P-quantisation diagnostic. */
+double fpo_e4m3_round(double x) {
+  double ax = fabs(x), best = 0.0, bestd = INFINITY;
+  int bestm = 0;
+  if (ax >= 448.0) return x < 0 ? -448.0 : 448.0;
+  for (int c = 0; c < 127; ++c) { /* 0x00..0x7e: every finite non-negative code */
+    double v = fpo_e4m3_decode((uint8_t)c);
+    double dd = fabs(v - ax);
+    int mant = c & 7;
+    if (dd < bestd || (dd == bestd && (mant & 1) == 0 && (bestm & 1) == 1)) {
+      bestd = dd;
+      best = v;
+      bestm = mant;
+    }
+  }
+  return x < 0 ? -best : best;
+}
+
+static double bf16_decode(uint16_t b) {
+  uint32_t bits = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+static double elem(const void* base, int dtype, size_t i, double c) {
+  switch (dtype) {
+    case FPO_F32: return (double)((const float*)base)[i];
+    case FPO_BF16: return bf16_decode(((const uint16_t*)base)[i]);
+    case FPO_E4M3: return c * fpo_e4m3_decode(((const uint8_t*)base)[i]);
+  }
+  return NAN;
+}
+
+/* Load one vector of length d. */
+static void load_q(const fpo_problem* p, int64_t row, int head, double* out) {
+  size_t base = ((size_t)row * p->hq + head) * p->d;
+  for (int i = 0; i < p->d; ++i) out[i] = elem(p->q, p->dtype, base + i, p->cq);
+}
+static void load_k(const fpo_problem* p, int64_t row, int head, double* out) {
+  size_t base = ((size_t)row * p->hkv + head) * p->d;
+  for (int i = 0; i < p->d; ++i) out[i] = elem(p->k, p->dtype, base + i, p->ck);
+}
+static void load_v(const fpo_problem* p, int64_t row, int head, double* out) {
+  size_t base = ((size_t)row * p->hkv + head) * p->d;
+  for (int i = 0; i < p->d; ++i) out[i] = elem(p->v, p->dtype, base + i, p->cv);
+}
+
+static double dot(const double* a, const double* b, int n) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += a[i] * b[i];
+  return s;
+}
+
+/* ------------------------------------------------------------------ */
+/* geometry                                                             */
+/* ------------------------------------------------------------------ */
+
+static int64_t req_len(const fpo_problem* p, int b) { return p->cu[b + 1] - p->cu[b]; }
+static int group(const fpo_problem* p) { return p->hq / p->hkv; }
+
+int64_t fpo_blocks_in_req(const fpo_problem* p, int b) {
+  return (req_len(p, b) + p->block - 1) / p->block;
+}
+
+/* first block of request b in the concatenated block list */
+int64_t fpo_block_offset(const fpo_problem* p, int b) {
+  int64_t off = 0;
+  for (int i = 0; i < b; ++i) off += fpo_blocks_in_req(p, i);
+  return off;
+}
+
+int64_t fpo_tiles_in_req(const fpo_problem* p, int b) {
+  int64_t packed = (int64_t)group(p) * req_len(p, b);
+  return (packed + p->rows - 1) / p->rows;
+}
+
+int64_t fpo_num_segments(const fpo_problem* p) {
+  int64_t n = 0;
+  for (int b = 0; b < p->num_reqs; ++b) n += (int64_t)p->hkv * fpo_tiles_in_req(p, b);
+  return n;
+}
+
+/* Segment s -> (request, kv head, tile); segments are ordered (b, h, I). */
+void fpo_segment_coords(const fpo_problem* p, int64_t s, int32_t* b_out, int32_t* h_out,
+                        int64_t* i_out) {
+  for (int b = 0; b < p->num_reqs; ++b) {
+    int64_t nt = fpo_tiles_in_req(p, b);
+    int64_t nb = (int64_t)p->hkv * nt;
+    if (s < nb) {
+      *b_out = b;
+      *h_out = (int32_t)(s / nt);
+      *i_out = s % nt;
+      return;
+    }
+    s -= nb;
+  }
+  *b_out = -1;
+  *h_out = -1;
+  *i_out = -1;
+}
+
+/* Tile I of (b, h): packed rows [I*R, min((I+1)R, g*L)), first/last position
+ * t0/t1 and its block beta = floor(t0/B) ([V2] §3.3 Eq. 13).  Returns the
+ * number of valid rows. */
+int fpo_tile_info(const fpo_problem* p, int b, int64_t I, int64_t* t0, int64_t* t1,
+                  int64_t* beta) {
+  int g = group(p);
+  int64_t packed = (int64_t)g * req_len(p, b);
+  int64_t r0 = I * p->rows;
+  int64_t r1 = r0 + p->rows;
+  if (r1 > packed) r1 = packed;
+  *t0 = r0 / g;
+  *t1 = (r1 - 1) / g;
+  *beta = *t0 / p->block;
+  return (int)(r1 - r0);
+}
+
+/* ------------------------------------------------------------------ */
+/* block mean pooling ([V2] §3.2 Eq. 5; §3.4 pipeline)                  */
+/* ------------------------------------------------------------------ */
+
+/* k_bar_J = (1/|B_J|) sum_{i in B_J} k_i, v_bar likewise, |B_J| = the actual
+ * number of tokens in block J (the last block of a request may be short).
+ * Output layout: [total_blocks][hkv][d], blocks concatenated by request. */
+void fpo_pool_all(const fpo_problem* p, double* kbar, double* vbar) {
+  int64_t nblk_total = fpo_block_offset(p, p->num_reqs);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t gb = 0; gb < nblk_total; ++gb) {
+    int b = 0;
+    int64_t J = gb;
+    while (J >= fpo_blocks_in_req(p, b)) J -= fpo_blocks_in_req(p, b++);
+    int64_t L = req_len(p, b);
+    int64_t lo = J * p->block, hi = lo + p->block;
+    if (hi > L) hi = L;
+    double n = (double)(hi - lo);
+    double* kv = (double*)malloc(sizeof(double) * p->d);
+    for (int h = 0; h < p->hkv; ++h) {
+      double* ko = kbar + ((size_t)gb * p->hkv + h) * p->d;
+      double* vo = vbar + ((size_t)gb * p->hkv + h) * p->d;
+      for (int i = 0; i < p->d; ++i) ko[i] = vo[i] = 0.0;
+      for (int64_t t = lo; t < hi; ++t) {
+        load_k(p, p->cu[b] + t, h, kv);
+        for (int i = 0; i < p->d; ++i) ko[i] += kv[i];
+        load_v(p, p->cu[b] + t, h, kv);
+        for (int i = 0; i < p->d; ++i) vo[i] += kv[i];
+      }
+      for (int i = 0; i < p->d; ++i) {
+        ko[i] /= n;
+        vo[i] /= n;
+      }
+    }
+    free(kv);
+  }
+}
+
+/* pooled row of block J of request b (whose first block is blk0) */
+static const double* kbar_row(const fpo_problem* p, const double* kbar, int64_t blk0, int h,
+                              int64_t J) {
+  return kbar + ((size_t)(blk0 + J) * p->hkv + h) * p->d;
+}
+
+/* ------------------------------------------------------------------ */
+/* block energies of one tile ([V2] §3.1 Eq. 1-3, §3.3 Eq. 19-20)        */
+/* ------------------------------------------------------------------ */
+
+/* Candidate blocks are J in [0, beta], the diagonal block included and scored
+ * with its full pooled mean (READING: the causal constraint of [V2] Eq. 3 and
+ * thresh = alpha * max_{J <= I} of [V1] §3.4).  The logit carries the softmax
+ * scale sigma as in [V2] Eq. 5 and Eq. 19 (READING: [V2] Eq. 1 omits it).
+ *
+ * form 0 -- direct: s_rJ = sigma q_r.k_bar_J, M = max_{r,J} s_rJ,
+ *           E_J = sum_r exp(s_rJ - M).
+ * form 1 -- [V2] Eq. 1-2 ([V1] §3.2): per-block max m_J over the tile rows,
+ *           S_J = sum_r exp(s_rJ - m_J), global M = max_J m_J,
+ *           E_J = S_J * exp(m_J - M).  Eq. 2's normalising sum and epsilon
+ *           cancel in the ratio of Eq. 3 and are not formed.
+ * form 2 -- [V2] Eq. 19-20: blocks visited in chunks of 64 with a running
+ *           log2-domain maximum M; E_J = sum_r 2^(s_rJ log2 e - M) with the
+ *           chunk's M stored as M_c; finally E_J <- E_J 2^(M_c - M_final).
+ *
+ * All forms return e_J = E_J / max_J' E_J' in (0, 1] (the normalised energy
+ * that [V2] Eq. 3 / Eq. 20 compare against alpha).  Returns beta + 1. */
+int64_t fpo_score_tile(const fpo_problem* p, const double* kbar, int b, int h, int64_t I,
+                       int form, double* e_out) {
+  int g = group(p);
+  int64_t t0, t1, beta;
+  int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
+  int64_t nc = beta + 1;
+  int d = p->d;
+  double* qv = (double*)malloc(sizeof(double) * (size_t)nrows * d);
+  double* s = (double*)malloc(sizeof(double) * (size_t)nrows * nc);
+  for (int r = 0; r < nrows; ++r) {
+    int64_t pr = I * p->rows + r;
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv + (size_t)r * d);
+  }
+  int64_t blk0 = fpo_block_offset(p, b);
+  for (int r = 0; r < nrows; ++r)
+    for (int64_t J = 0; J < nc; ++J)
+      s[(size_t)r * nc + J] = p->scale * dot(qv + (size_t)r * d, kbar_row(p, kbar, blk0, h, J), d);
+
+  if (form == 0) {
+    double M = -INFINITY;
+    for (size_t i = 0; i < (size_t)nrows * nc; ++i)
+      if (s[i] > M) M = s[i];
+    for (int64_t J = 0; J < nc; ++J) {
+      double E = 0.0;
+      for (int r = 0; r < nrows; ++r) E += exp(s[(size_t)r * nc + J] - M);
+      e_out[J] = E;
+    }
+  } else if (form == 1) {
+    double* m = (double*)malloc(sizeof(double) * nc);
+    double Mi = -INFINITY;
+    for (int64_t J = 0; J < nc; ++J) {
+      m[J] = -INFINITY;
+      for (int r = 0; r < nrows; ++r)
+        if (s[(size_t)r * nc + J] > m[J]) m[J] = s[(size_t)r * nc + J];
+      if (m[J] > Mi) Mi = m[J];
+    }
+    for (int64_t J = 0; J < nc; ++J) {
+      double S = 0.0;
+      for (int r = 0; r < nrows; ++r) S += exp(s[(size_t)r * nc + J] - m[J]);
+      e_out[J] = S * exp(m[J] - Mi);
+    }
+    free(m);
+  } else {
+    const double LOG2E = 1.0 / log(2.0);
+    const int64_t CH = 64;
+    int64_t nchunks = (nc + CH - 1) / CH;
+    double* Mc = (double*)malloc(sizeof(double) * nchunks);
+    double M = -INFINITY;
+    for (int64_t c = 0; c < nchunks; ++c) {
+      int64_t j0 = c * CH, j1 = j0 + CH < nc ? j0 + CH : nc;
+      double Mt = -INFINITY;
+      for (int r = 0; r < nrows; ++r)
+        for (int64_t J = j0; J < j1; ++J)
+          if (s[(size_t)r * nc + J] * LOG2E > Mt) Mt = s[(size_t)r * nc + J] * LOG2E;
+      if (Mt > M) M = Mt;
+      Mc[c] = M;
+      for (int64_t J = j0; J < j1; ++J) {
+        double E = 0.0;
+        for (int r = 0; r < nrows; ++r) E += exp2(s[(size_t)r * nc + J] * LOG2E - M);
+        e_out[J] = E;
+      }
+    }
+    for (int64_t J = 0; J < nc; ++J) e_out[J] *= exp2(Mc[J / CH] - M);
+    free(Mc);
+  }
+  double Emax = 0.0;
+  for (int64_t J = 0; J < nc; ++J)
+    if (e_out[J] > Emax) Emax = e_out[J];
+  for (int64_t J = 0; J < nc; ++J) e_out[J] /= Emax;
+  free(qv);
+  free(s);
+  return nc;
+}
+
+/* ------------------------------------------------------------------ */
+/* max-based threshold with forced blocks ([V2] Eq. 3, Eq. 20)          */
+/* ------------------------------------------------------------------ */
+
+/* Keep J iff e_J >= alpha (inclusive), or J is a sink block (J < n_sink), a
+ * window block (the n_win blocks just before beta), or the diagonal block
+ * beta ([V2] §3.1 "Max-based Dynamic Thresholding"; defaults in §4.1).
+ * ambig[J] marks unforced blocks with |e_J - alpha| <= 1e-4 alpha, where two
+ * correct implementations may legitimately disagree. */
+void fpo_select_tile(const double* e, int64_t nc, double alpha, int n_sink, int n_win,
+                     uint8_t* sel, uint8_t* ambig) {
+  int64_t beta = nc - 1;
+  for (int64_t J = 0; J < nc; ++J) {
+    int forced = (J < n_sink) || (J >= beta - n_win && J < beta) || (J == beta);
+    sel[J] = (uint8_t)(forced || e[J] >= alpha);
+    if (ambig) ambig[J] = (uint8_t)(!forced && fabs(e[J] - alpha) <= 1e-4 * alpha);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* CSR segment ([V2] §3.3 Eq. 17; logical-to-physical expansion, §3.4)   */
+/* ------------------------------------------------------------------ */
+
+/* Each selected logical block J becomes the B/P physical tiles J*(B/P)+k, in
+ * ascending order.  READING: a tile p whose first key P*p lies after the
+ * tile's last position t1 holds no visible key for any row and is dropped. */
+int64_t fpo_csr_tile(const uint8_t* sel, int64_t nc, int64_t t1, int phys, int block,
+                     int32_t* out) {
+  int64_t n = 0;
+  int per = block / phys;
+  for (int64_t J = 0; J < nc; ++J) {
+    if (!sel[J]) continue;
+    for (int k = 0; k < per; ++k) {
+      int64_t tile = J * per + k;
+      if (tile * phys > t1) continue;
+      if (out) out[n] = (int32_t)tile;
+      ++n;
+    }
+  }
+  return n;
+}
+
+/* Whole-problem index: cu[n_seg+1] (exclusive prefix sum in segment order)
+ * and idx.  e_out / ambig_out (optional) are [n_seg][max_nc] with max_nc the
+ * largest beta+1, padded with -1 / 0.  Returns the number of idx entries, or
+ * -1 if cap is too small. */
+int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, int n_sink,
+                       int n_win, int form, int32_t* cu, int32_t* idx, int64_t cap,
+                       double* e_out, uint8_t* ambig_out, int64_t max_nc) {
+  int64_t nseg = fpo_num_segments(p);
+  int64_t* counts = (int64_t*)malloc(sizeof(int64_t) * (nseg + 1));
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t s = 0; s < nseg; ++s) {
+    int32_t b, h;
+    int64_t I, t0, t1, beta;
+    fpo_segment_coords(p, s, &b, &h, &I);
+    fpo_tile_info(p, b, I, &t0, &t1, &beta);
+    int64_t nc = beta + 1;
+    double* e = (double*)malloc(sizeof(double) * nc);
+    uint8_t* sel = (uint8_t*)malloc(nc);
+    uint8_t* amb = (uint8_t*)malloc(nc);
+    fpo_score_tile(p, kbar, b, h, I, form, e);
+    fpo_select_tile(e, nc, alpha, n_sink, n_win, sel, amb);
+    counts[s] = fpo_csr_tile(sel, nc, t1, p->phys, p->block, NULL);
+    if (e_out)
+      for (int64_t J = 0; J < max_nc; ++J) e_out[s * max_nc + J] = J < nc ? e[J] : -1.0;
+    if (ambig_out)
+      for (int64_t J = 0; J < max_nc; ++J) ambig_out[s * max_nc + J] = J < nc ? amb[J] : 0;
+    free(e);
+    free(sel);
+    free(amb);
+  }
+  int64_t total = 0;
+  for (int64_t s = 0; s < nseg; ++s) {
+    int64_t c = counts[s];
+    counts[s] = total;
+    total += c;
+  }
+  counts[nseg] = total;
+  for (int64_t s = 0; s <= nseg; ++s) cu[s] = (int32_t)counts[s];
+  if (total > cap) {
+    free(counts);
+    return -1;
+  }
+#pragma omp parallel for schedule(dynamic, 8)
+  for (int64_t s = 0; s < nseg; ++s) {
+    int32_t b, h;
+    int64_t I, t0, t1, beta;
+    fpo_segment_coords(p, s, &b, &h, &I);
+    fpo_tile_info(p, b, I, &t0, &t1, &beta);
+    int64_t nc = beta + 1;
+    double* e = (double*)malloc(sizeof(double) * nc);
+    uint8_t* sel = (uint8_t*)malloc(nc);
+    fpo_score_tile(p, kbar, b, h, I, form, e);
+    fpo_select_tile(e, nc, alpha, n_sink, n_win, sel, NULL);
+    fpo_csr_tile(sel, nc, t1, p->phys, p->block, idx + counts[s]);
+    free(e);
+    free(sel);
+  }
+  free(counts);
+  return total;
+}
+
+/* ------------------------------------------------------------------ */
+/* attention of one tile with mean correction ([V2] §3.2 Eq. 4-6)       */
+/* ------------------------------------------------------------------ */
+
+/* For every valid row r of tile I (position t = floor(r/g)):
+ *   exact tokens  T = { i <= t : floor(i/P) in idx }
+ *   selected blocks S = { floor(p P / B) : p in idx }
+ *   corrected blocks C = { J < beta : J not in S } when correction is on:
+ *     the blocks fully visible to every row of the tile ([V2] §3.2
+ *     "Implementation"); each stands for |B_J| = B tokens.
+ *   logits a_i = sigma q.k_i (i in T), c_J = sigma q.k_bar_J + ln|B_J| (J in C)
+ *   O = (sum_T e^{a_i-m} v_i + sum_C e^{c_J-m} v_bar_J) / (sum_T e^{a_i-m} + sum_C e^{c_J-m})
+ *   LSE = m + ln(denominator), m = max of all logits.
+ * p8 != 0 is a diagnostic of [V2] Eq. 15: every weight e^{a-m} is multiplied by
+ * 2^8 and rounded to E4M3 before both sums, and LSE subtracts ln 2^8.
+ * out is [R][d], lse is [R]; rows past the end of the request are zeroed. */
+void fpo_attend_tile(const fpo_problem* p, const double* kbar, const double* vbar, int b,
+                     int h, int64_t I, const int32_t* idx, int64_t T, int correction, int p8,
+                     double* out, double* lse) {
+  int g = group(p), d = p->d;
+  int64_t t0, t1, beta;
+  int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
+  int64_t L = req_len(p, b);
+  int64_t nblk = fpo_blocks_in_req(p, b);
+  int64_t blk0 = fpo_block_offset(p, b);
+  uint8_t* in_s = (uint8_t*)calloc((size_t)nblk, 1);
+  for (int64_t t = 0; t < T; ++t) {
+    int64_t J = (int64_t)idx[t] * p->phys / p->block;
+    if (J >= 0 && J < nblk) in_s[J] = 1;
+  }
+  double* qv = (double*)malloc(sizeof(double) * d);
+  double* kv = (double*)malloc(sizeof(double) * d);
+  double* vv = (double*)malloc(sizeof(double) * d);
+  double* num = (double*)malloc(sizeof(double) * d);
+  for (int r = 0; r < p->rows; ++r) {
+    double* o = out + (size_t)r * d;
+    if (r >= nrows) {
+      for (int i = 0; i < d; ++i) o[i] = 0.0;
+      if (lse) lse[r] = 0.0;
+      continue;
+    }
+    int64_t pr = I * p->rows + r;
+    int64_t t = pr / g;
+    load_q(p, p->cu[b] + t, h * g + (int)(pr % g), qv);
+    /* pass 1: the row maximum over every logit that enters the softmax */
+    double m = -INFINITY;
+    for (int64_t e = 0; e < T; ++e)
+      for (int64_t i = (int64_t)idx[e] * p->phys; i < ((int64_t)idx[e] + 1) * p->phys; ++i) {
+        if (i > t || i >= L) continue;
+        load_k(p, p->cu[b] + i, h, kv);
+        double a = p->scale * dot(qv, kv, d);
+        if (a > m) m = a;
+      }
+    if (correction)
+      for (int64_t J = 0; J < beta; ++J) {
+        if (in_s[J]) continue;
+        double c = p->scale * dot(qv, kbar_row(p, kbar, blk0, h, J), d) + log((double)p->block);
+        if (c > m) m = c;
+      }
+    /* pass 2: numerator and denominator of [V2] Eq. 6 */
+    double den = 0.0;
+    for (int i = 0; i < d; ++i) num[i] = 0.0;
+    for (int64_t e = 0; e < T; ++e)
+      for (int64_t i = (int64_t)idx[e] * p->phys; i < ((int64_t)idx[e] + 1) * p->phys; ++i) {
+        if (i > t || i >= L) continue;
+        load_k(p, p->cu[b] + i, h, kv);
+        load_v(p, p->cu[b] + i, h, vv);
+        double w = exp(p->scale * dot(qv, kv, d) - m);
+        if (p8) w = fpo_e4m3_round(256.0 * w);
+        den += w;
+        for (int j = 0; j < d; ++j) num[j] += w * vv[j];
+      }
+    if (correction)
+      for (int64_t J = 0; J < beta; ++J) {
+        if (in_s[J]) continue;
+        const double* kb = kbar_row(p, kbar, blk0, h, J);
+        const double* vb = kbar_row(p, vbar, blk0, h, J);
+        double w = exp(p->scale * dot(qv, kb, d) + log((double)p->block) - m);
+        if (p8) w = fpo_e4m3_round(256.0 * w);
+        den += w;
+        for (int j = 0; j < d; ++j) num[j] += w * vb[j];
+      }
+    for (int j = 0; j < d; ++j) o[j] = num[j] / den;
+    if (lse) lse[r] = m + log(den) - (p8 ? log(256.0) : 0.0);
+  }
+  free(in_s);
+  free(qv);
+  free(kv);
+  free(vv);
+  free(num);
+}
+
+/* Dense causal softmax attention of the same rows ([V2] §3.2 Eq. 4 left). */
+void fpo_dense_tile(const fpo_problem* p, int b, int h, int64_t I, double* out, double* lse) {
+  int g = group(p), d = p->d;
+  int64_t t0, t1, beta;
+  int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
+  double* qv = (double*)malloc(sizeof(double) * d);
+  double* kv = (double*)malloc(sizeof(double) * d);
+  double* vv = (double*)malloc(sizeof(double) * d);
+  double* num = (double*)malloc(sizeof(double) * d);
+  for (int r = 0; r < p->rows; ++r) {
+    double* o = out + (size_t)r * d;
+    if (r >= nrows) {
+      for (int i = 0; i < d; ++i) o[i] = 0.0;
+      if (lse) lse[r] = 0.0;
+      continue;
+    }
+    int64_t pr = I * p->rows + r;
+    int64_t t = pr / g;
+    load_q(p, p->cu[b] + t, h * g + (int)(pr % g), qv);
+    double m = -INFINITY;
+    for (int64_t i = 0; i <= t; ++i) {
+      load_k(p, p->cu[b] + i, h, kv);
+      double a = p->scale * dot(qv, kv, d);
+      if (a > m) m = a;
+    }
+    double den = 0.0;
+    for (int i = 0; i < d; ++i) num[i] = 0.0;
+    for (int64_t i = 0; i <= t; ++i) {
+      load_k(p, p->cu[b] + i, h, kv);
+      load_v(p, p->cu[b] + i, h, vv);
+      double w = exp(p->scale * dot(qv, kv, d) - m);
+      den += w;
+      for (int j = 0; j < d; ++j) num[j] += w * vv[j];
+    }
+    for (int j = 0; j < d; ++j) o[j] = num[j] / den;
+    if (lse) lse[r] = m + log(den);
+  }
+  free(qv);
+  free(kv);
+  free(vv);
+  free(num);
+}
+
+/* Batch drivers over a list of segment ids (OpenMP over segments).
+ * mode 0: sparse with the given CSR (cu, idx indexed by segment id);
+ * mode 1: dense.  out is [nlist][R][d], lse is [nlist][R]. */
+void fpo_attend_list(const fpo_problem* p, const double* kbar, const double* vbar,
+                     int64_t nlist, const int64_t* segs, const int32_t* cu, const int32_t* idx,
+                     int mode, int correction, int p8, double* out, double* lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nlist; ++n) {
+    int32_t b, h;
+    int64_t I;
+    fpo_segment_coords(p, segs[n], &b, &h, &I);
+    double* o = out + (size_t)n * p->rows * p->d;
+    double* l = lse ? lse + (size_t)n * p->rows : NULL;
+    if (mode == 1)
+      fpo_dense_tile(p, b, h, I, o, l);
+    else
+      fpo_attend_tile(p, kbar, vbar, b, h, I, idx + cu[segs[n]], cu[segs[n] + 1] - cu[segs[n]],
+                      correction, p8, o, l);
+  }
+}
+
+int fpo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
