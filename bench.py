@@ -1,0 +1,274 @@
+"""Benchmark of the block-sparse prefill path on one MI355X.
+
+One step = the whole hot path over one batch: fp_select (pooling, scoring,
+selection, CSR) + fp_sparse_attn (sparse attention with mean correction), on
+the 128K-token Qwen3-30B-A3B-shaped layer (Hq=32, Hkv=4, d=128, bf16,
+alpha=0.1, 2 sink + 4 window blocks).  Inputs are seeded synthetic tensors
+already resident in HBM.  Prints ONE JSON line.
+
+  value      effective dense-equivalent TFLOP/s = 2 d Hq sum L(L+1) / t_step
+  roofline   the attention kernel's algorithmic FLOP rate vs the bf16 MFMA peak
+  extra      per-stage times, the dense baseline on the same kernel, FP8 and
+             alpha / correction variants, density
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_long_mean_amd import configs, synth  # noqa: E402
+
+METRIC = "128K sparse-prefill attn ms, eff. TFLOP/s (bf16/fp8), MFMA util vs peak"
+PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI355X
+D = 128
+
+
+def dense_flops(lengths, hq):
+    return float(sum(2.0 * D * hq * L * (L + 1) for L in lengths))
+
+
+def csr_work(lengths, hq, hkv, cu, idx, correction):
+    """Algorithmic and executed attention FLOPs of a CSR (host arithmetic on the index).
+
+    algorithmic: 4 d per (packed row, visible key in a listed tile) + 4 d per
+    (packed row, corrected block); executed: 4 d x 128 rows x 64 per step the
+    kernel runs (listed tiles + correction chunks with something to correct)."""
+    g = hq // hkv
+    alg = 0.0
+    steps = 0
+    nsel_blocks = 0
+    ncand = 0
+    s = 0
+    for L in lengths:
+        nt = -(-g * L // 128)
+        for h in range(hkv):
+            for I in range(nt):
+                r0, r1 = I * 128, min((I + 1) * 128, g * L)
+                pos = np.arange(r0, r1) // g
+                t0 = r0 // g
+                beta = t0 // 128
+                lst = idx[cu[s]:cu[s + 1]]
+                full = int(np.count_nonzero(lst < 2 * beta))
+                keys = 64 * full + np.zeros(len(pos))
+                for p in (2 * beta, 2 * beta + 1):
+                    if np.any(lst == p):
+                        keys += np.clip(pos - 64 * p + 1, 0, 64)
+                blocks = np.unique(lst // 2)
+                sel_before = int(np.count_nonzero(blocks < beta))
+                corr = (beta - sel_before) if correction else 0
+                alg += 4.0 * D * float(keys.sum() + corr * len(pos))
+                st = len(lst)
+                if correction and beta > 0:
+                    selmask = np.zeros(beta, bool)
+                    selmask[blocks[blocks < beta]] = True
+                    for c0 in range(0, beta, 64):
+                        if not selmask[c0:c0 + 64].all():
+                            st += 1
+                steps += st
+                nsel_blocks += len(blocks)
+                ncand += beta + 1
+                s += 1
+    execd = 4.0 * D * 128 * 64 * steps
+    return alg, execd, nsel_blocks / max(1, ncand)
+
+
+def time_calls(fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+class Case:
+    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4):
+        from block_sparse_long_mean_amd import fp
+
+        self.fp = fp
+        self.batch = batch
+        tdt = {"bf16": torch.bfloat16, "e4m3": torch.uint8, "f32": torch.float32}[batch.dtype]
+        self.q = batch.q.cuda()
+        if paged is None:
+            self.k, self.v = batch.k.cuda(), batch.v.cuda()
+            self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt,
+                                   descale=batch.descale if batch.dtype == "e4m3" else None)
+        else:
+            self.k, self.v = paged.k_pool.cuda(), paged.v_pool.cuda()
+            self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt, page_table=paged.page_table,
+                                   page_size=paged.page_size, num_pool_slots=paged.num_slots,
+                                   descale=batch.descale if batch.dtype == "e4m3" else None)
+        self.params = fp.select_params(alpha, sink, win)
+        self.bufs = fp.Buffers(self.B, self.params)
+        odt = torch.float32 if batch.dtype == "f32" else torch.bfloat16
+        self.out = torch.empty((batch.total, batch.hq, D), dtype=odt, device="cuda")
+        self.lse = torch.empty((batch.total, batch.hq), dtype=torch.float32, device="cuda")
+
+    def select(self):
+        self.fp.select(self.B, self.params, self.q, self.k, self.v, self.bufs)
+
+    def attn(self, correction=True):
+        self.fp.sparse_attn(self.B, self.params, self.q, self.k, self.v, self.bufs, self.out, self.lse,
+                            correction=correction)
+
+    def dense(self):
+        self.fp.dense_attn(self.B, self.q, self.k, self.v, self.bufs, self.out, self.lse)
+
+    def csr(self):
+        torch.cuda.synchronize()
+        cu = self.bufs.cu.cpu().numpy()
+        return cu, self.bufs.idx[: int(cu[-1])].cpu().numpy()
+
+
+def measure(case, steps, warmup, correction=True):
+    sel = time_calls(case.select, steps, warmup)
+    att = time_calls(lambda: case.attn(correction), steps, warmup)
+    cu, idx = case.csr()
+    b = case.batch
+    alg, execd, density = csr_work(b.lengths, b.hq, b.hkv, cu, idx, correction)
+    sel_ms, att_ms = float(np.median(sel)), float(np.median(att))
+    return {"select_ms": sel_ms, "attn_ms": att_ms, "step_ms": sel_ms + att_ms, "density": density,
+            "attn_alg_flop": alg, "attn_exec_flop": execd, "csr_entries": int(len(idx)),
+            "csr_mib": len(idx) * 4 / 2**20}
+
+
+def cpu_baseline(batch, w, n_seg=64):
+    """The oracle (fp64, OpenMP over segments) on a bounded sample: pooling of every
+    block, then scoring, selection and mean-corrected attention of n_seg segments."""
+    import oracle
+    from tests.helpers import oracle_problem
+
+    P = oracle_problem(batch)
+    t0 = time.time()
+    P.pool()
+    t_pool = time.time() - t0
+    nseg = P.num_segments()
+    rng = np.random.default_rng(0)
+    segs = sorted(2 * x for x in rng.choice(nseg // 2, size=n_seg, replace=False).tolist())  # non-adjacent
+    t1 = time.time()
+    cu = np.zeros(nseg + 1, np.int32)
+    lists = []
+    off = 0
+    for s in segs:
+        e, sel, amb, lst = P.segment_select(s, w.alpha, w.sink_blocks, w.window_blocks)
+        cu[s], cu[s + 1] = off, off + len(lst)
+        off += len(lst)
+        lists.append(lst)
+    P.attend_segments(segs, cu, np.concatenate(lists), correction=True)
+    t_seg = time.time() - t1
+    flops = 0.0
+    for s in segs:
+        b, _, _ = P.segment_coords(s)
+        pos, _, valid = P.rows_of_segment(s)
+        flops += float(np.sum(4.0 * D * (pos[valid] - P.cu[b] + 1)))
+    # dense-equivalent rate of the sampled rows, charging the pooling pro rata
+    total_rows = batch.total * batch.hq
+    sample_rows = n_seg * 128
+    t = t_seg + t_pool * sample_rows / total_rows
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_seg} of {nseg} (KV head, query tile) segments: scoring and selection "
+                      f"(serial) and mean-corrected attention (OpenMP), plus pooling of all blocks "
+                      f"charged pro rata (pool {t_pool:.1f} s, segments {t_seg:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=configs.L128K.name, choices=sorted(configs.ALL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip dense / fp8 / alpha variants")
+    ap.add_argument("--cpu-segments", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    w = configs.ALL[args.config]
+    t0 = time.time()
+    batch, paged = w.make()
+    gen_s = time.time() - t0
+    case = Case(batch, paged, w.alpha, w.sink_blocks, w.window_blocks)
+    main_m = measure(case, args.steps, args.warmup, correction=True)
+    F = dense_flops(batch.lengths, batch.hq)
+    peak = PEAK[batch.dtype]
+    attn_s = main_m["attn_ms"] / 1e3
+    achieved = main_m["attn_alg_flop"] / attn_s / 1e12
+    extra = {
+        "select_ms": main_m["select_ms"], "sparse_attn_ms": main_m["attn_ms"],
+        "density": main_m["density"], "csr_mib": main_m["csr_mib"],
+        "attn_alg_tflop": main_m["attn_alg_flop"] / 1e12, "attn_exec_tflop": main_m["attn_exec_flop"] / 1e12,
+        "mfma_util_executed": main_m["attn_exec_flop"] / attn_s / 1e12 / peak,
+        "dense_equiv_tflop": F / 1e12, "input_gen_s": gen_s,
+    }
+    if not args.no_extra:
+        d_ms = float(np.median(time_calls(case.dense, 3, 1)))
+        extra["dense_ms"] = d_ms
+        extra["dense_tflops"] = F / (d_ms / 1e3) / 1e12
+        extra["dense_mfma_util"] = extra["dense_tflops"] / peak
+        extra["speedup_vs_dense"] = d_ms / main_m["step_ms"]
+        variants = {}
+        m = measure(case, 3, 1, correction=False)
+        variants["alpha0.1_nocorr"] = {k: m[k] for k in ("select_ms", "attn_ms", "step_ms", "density")}
+        c2 = Case(batch, paged, 0.2, w.sink_blocks, w.window_blocks)
+        for corr in (True, False):
+            m = measure(c2, 3, 1, correction=corr)
+            variants[f"alpha0.2_{'corr' if corr else 'nocorr'}"] = {
+                k: m[k] for k in ("select_ms", "attn_ms", "step_ms", "density")}
+        del c2
+        if batch.dtype == "bf16" and w.page_size == 0:
+            b8 = synth.to_e4m3(batch)
+            for a in (0.1, 0.2):
+                c8 = Case(b8, None, a, w.sink_blocks, w.window_blocks)
+                m = measure(c8, 5, 2, correction=True)
+                variants[f"fp8_alpha{a}"] = {
+                    "select_ms": m["select_ms"], "attn_ms": m["attn_ms"], "step_ms": m["step_ms"],
+                    "density": m["density"], "eff_tflops": F / (m["step_ms"] / 1e3) / 1e12,
+                    "attn_alg_tflops": m["attn_alg_flop"] / (m["attn_ms"] / 1e3) / 1e12,
+                    "mfma_util_executed": m["attn_exec_flop"] / (m["attn_ms"] / 1e3) / 1e12 / PEAK["e4m3"]}
+                if a == 0.1:
+                    dd = float(np.median(time_calls(c8.dense, 3, 1)))
+                    variants["fp8_dense_ms"] = dd
+                    variants["fp8_speedup_vs_dense"] = dd / m["step_ms"]
+                del c8
+        extra["variants"] = variants
+    res = {
+        "metric": METRIC,
+        "value": F / (main_m["step_ms"] / 1e3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": main_m["step_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": batch.dtype, "data": "synthetic (seeded generator standing in for RULER needle-in-a-haystack)",
+        "config": {"workload": w.name, "lengths": list(batch.lengths)[:4] + (["..."] if len(batch.lengths) > 4 else []),
+                   "num_reqs": len(batch.lengths), "hq": batch.hq, "hkv": batch.hkv, "d": D, "alpha": w.alpha,
+                   "sink_blocks": w.sink_blocks, "window_blocks": w.window_blocks,
+                   "paged": bool(w.page_size), "mean_correction": True},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (fp_sparse_attn)", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(batch, w, args.cpu_segments)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,641 @@
+// attn.hip -- attention stage: persistent MFMA flash attention over the CSR
+// index with mean-correction steps, the dense causal baseline on the same
+// mainloop, and the combine of KV splits.
+//
+// Method ([V2] §3.2 Eq. 6, §3.3): for each query tile (128 PackGQA rows of one
+// KV head, Eq. 12-13) the listed 64-key tiles are visited backwards
+// (n_t = idx[cu + T - 1 - t], Eq. 17) with an online softmax; every block
+// J < beta that no listed tile covers is then folded in as one extra step
+// whose "keys" are pooled means: logit sigma q.kbar_J + ln 128, value
+// vbar_J ([V2] §3.2 "Implementation"), 64 blocks per step, blocks that are
+// selected or not fully visible masked out.  Under KV splitting a unit takes
+// the contiguous count range [u ceil(W/U), (u+1) ceil(W/U)) of its W steps
+// (Eq. 18) and partial results are merged by log-sum-exp in split order.
+//
+// MI355X mapping.  A workgroup is 4 waves x 32 query rows.  Logits are
+// computed transposed, S^T = K Q^T (A = K tile from LDS, B = the wave's Q rows
+// held in registers), so each lane owns one query row: row max and row sum
+// are in-lane plus one exchange with lane^32, and the probabilities land in
+// exactly the register layout of the B operand of O^T += V^T P^T.  V is
+// therefore staged in LDS transposed, with its key order permuted to match
+// that register layout.  K/V tiles are gathered through the page table
+// ([V2] Eq. 22) with 8-element vector loads into registers one step ahead of
+// the MFMAs and written to the other half of a double-buffered LDS stage.
+// The persistent grid pulls work units, sorted by descending work on the
+// device, from an atomic counter.  bf16: v_mfma_f32_32x32x16_bf16; e4m3:
+// v_mfma_scale_f32_32x32x64_f8f6f4 with P quantised as e4m3(2^8 e^{s-m})
+// ([V2] Eq. 15); fp32: v_mfma_f32_32x32x2f32.
+#include "device_common.h"
+
+namespace fp {
+
+template <int DT>
+struct Tr;
+template <>
+struct Tr<kBF16> {
+  static constexpr int KPL = 8;  // contraction elements per lane per MFMA
+  static constexpr int EB = 2;
+  using Op = bf16x8;
+};
+template <>
+struct Tr<kE4M3> {
+  static constexpr int KPL = 32;
+  static constexpr int EB = 1;
+  using Op = i32x8;
+};
+template <>
+struct Tr<kF32> {
+  static constexpr int KPL = 1;
+  static constexpr int EB = 4;
+  using Op = float;
+};
+
+// One MFMA operand (KPL elements) from LDS, read in 16-byte pieces.
+template <int DT>
+__device__ __forceinline__ typename Tr<DT>::Op lds_op(const char* p) {
+  if constexpr (DT == kBF16) {
+    return __builtin_bit_cast(bf16x8, *(const uint4*)p);
+  } else if constexpr (DT == kE4M3) {
+    uint4 a = ((const uint4*)p)[0], b = ((const uint4*)p)[1];
+    i32x8 r;
+    r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+    r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+    return r;
+  } else {
+    return *(const float*)p;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mma(typename Tr<DT>::Op a, typename Tr<DT>::Op b, f32x16 c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else if constexpr (DT == kE4M3)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int DT>
+struct Cfg {
+  static constexpr int EB = Tr<DT>::EB;
+  static constexpr int KPL = Tr<DT>::KPL;
+  static constexpr int KPITCH = kD * EB + 16;    // bytes per staged K row
+  static constexpr int VPITCH = kTile * EB + 16; // bytes per staged V^T row
+  static constexpr int KBYTES = kTile * KPITCH;
+  static constexpr int VBYTES = kD * VPITCH;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int LDS = 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
+  static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
+  static constexpr int NM1 = kTile / (2 * KPL);  // MFMAs per 32-column output tile
+  static constexpr int WGS = DT == kF32 ? 1 : 2; // workgroups per CU
+};
+
+// Position in a staged V^T row of key j (0..63) of the tile: keys are laid
+// out in the order in which each lane half holds the probabilities of the
+// two 32x32 logit tiles (key = 32 jt + 8 (r/4) + 4 half + r%4 for register r).
+template <int KPL>
+__device__ __forceinline__ int vt_pos(int j) {
+  int jt = j >> 5, jj = j & 31;
+  int half = (jj >> 2) & 1;
+  int r = ((jj >> 3) << 2) | (jj & 3);
+  int id = jt * 16 + r;
+  return (id / KPL) * (2 * KPL) + half * KPL + (id % KPL);
+}
+
+// 8 consecutive elements (raw storage) of one K/V/mean row.
+template <int DT>
+struct Vec8 {
+  static constexpr int W = 8 * Tr<DT>::EB / 4;  // dwords
+  uint32_t w[W];
+};
+
+template <int DT>
+__device__ __forceinline__ void ld8(Vec8<DT>& o, const char* p) {
+  if constexpr (DT == kBF16) {
+    uint4 a = *(const uint4*)p;
+    o.w[0] = a.x; o.w[1] = a.y; o.w[2] = a.z; o.w[3] = a.w;
+  } else if constexpr (DT == kE4M3) {
+    uint2 a = *(const uint2*)p;
+    o.w[0] = a.x; o.w[1] = a.y;
+  } else {
+    uint4 a = ((const uint4*)p)[0], b = ((const uint4*)p)[1];
+    o.w[0] = a.x; o.w[1] = a.y; o.w[2] = a.z; o.w[3] = a.w;
+    o.w[4] = b.x; o.w[5] = b.y; o.w[6] = b.z; o.w[7] = b.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void zero8(Vec8<DT>& o) {
+#pragma unroll
+  for (int i = 0; i < Vec8<DT>::W; ++i) o.w[i] = 0;
+}
+
+// element e (0..7) of a Vec8 as raw bits
+template <int DT>
+__device__ __forceinline__ uint32_t el(const Vec8<DT>& o, int e) {
+  if constexpr (DT == kBF16)
+    return (o.w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+  else if constexpr (DT == kE4M3)
+    return (o.w[e >> 2] >> (8 * (e & 3))) & 0xffu;
+  else
+    return o.w[e];
+}
+
+struct Unit {
+  int64_t s;
+  int split, nsplit;
+};
+
+template <int DT, bool DENSE>
+__global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
+    Geo g, WsLayout wl, char* __restrict__ ws, MeansLayout ml, const void* __restrict__ q,
+    const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ idx, const char* __restrict__ means, int correction,
+    void* __restrict__ out, float* __restrict__ lse) {
+  using C = Cfg<DT>;
+  using Op = typename Tr<DT>::Op;
+  constexpr int KPL = C::KPL;
+  extern __shared__ __align__(16) char smem[];
+  uint32_t* selbits = (uint32_t*)(smem + 2 * C::STAGE);
+  __shared__ int sh_unit;
+  __shared__ int sh_bad;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int2* units = (const int2*)(ws + wl.units);
+  const float sl = g.scale * 1.4426950408889634f *
+                   (DT == kE4M3 ? g.descale[0] * g.descale[1] : 1.f);
+  const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
+
+  for (;;) {
+    if (tid == 0) {
+      int u = atomicAdd(&g.hdr->work_counter, 1);
+      sh_unit = u;
+      sh_bad = 0;
+    }
+    __syncthreads();
+    const int u = sh_unit;
+    if (u >= g.hdr->total_units) break;
+    const int2 ud = units[u];
+    Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
+    const SegCoord c = seg_coord(g, un.s);
+    const TileGeo t = tile_geo(g, c);
+    int T, seg0 = 0;
+    if constexpr (DENSE) {
+      T = t.t1 / kTile + 1;
+    } else {
+      seg0 = cu[un.s];
+      T = cu[un.s + 1] - seg0;
+      if (T < 0 || T > 2 * (t.beta + 1)) {
+        if (tid == 0) { atomicOr(&g.hdr->err, kErrIdx); sh_bad = 1; }
+        T = 0;
+      }
+    }
+    const int NC = (!DENSE && correction) ? (t.beta + kChunk - 1) / kChunk : 0;
+    const int W = T + NC;
+    const int per = (W + un.nsplit - 1) / un.nsplit;
+    const int it0 = min(W, un.split * per), it1 = min(W, it0 + per);
+
+    if (NC > 0) {
+      for (int w = tid; w <= (t.beta >> 5); w += 256) selbits[w] = 0;
+      __syncthreads();
+      for (int e = tid; e < T; e += 256) {
+        int p = idx[seg0 + e];
+        int J = p / 2;
+        if (J >= 0 && J < t.beta) atomicOr(&selbits[J >> 5], 1u << (J & 31));
+      }
+    }
+    __syncthreads();
+
+    // ---- the wave's 32 query rows as the B operand of S^T = K Q^T
+    const int row_in_tile = wave * 32 + col;
+    const bool row_ok = row_in_tile < t.nrows;
+    const int64_t prow = c.I * kRows + row_in_tile;
+    const int pos = (int)(prow >> g.log2g);
+    const int head = c.h * g.g + (int)(prow & (g.g - 1));
+    const int64_t qrow = (c.row0 + pos) * g.hq + head;
+    Op qf[C::NM0];
+#pragma unroll
+    for (int m = 0; m < C::NM0; ++m) {
+      const int d0 = m * 2 * KPL + half * KPL;
+      if constexpr (DT == kBF16) {
+        uint4 w = row_ok ? *(const uint4*)((const uint16_t*)q + qrow * kD + d0) : make_uint4(0, 0, 0, 0);
+        qf[m] = __builtin_bit_cast(bf16x8, w);
+      } else if constexpr (DT == kE4M3) {
+        i32x8 w = {};
+        if (row_ok) {
+          const uint4* p = (const uint4*)((const uint8_t*)q + qrow * kD + d0);
+          uint4 a = p[0], b = p[1];
+          w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+          w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        }
+        qf[m] = w;
+      } else {
+        qf[m] = row_ok ? ((const float*)q)[qrow * kD + d0] : 0.f;
+      }
+    }
+
+    float m_i = -INFINITY, l_i = 0.f;
+    f32x16 oacc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) oacc[nt] = f32x16{};
+
+    // ---- step descriptors: tiles (backwards through the list), then chunks
+    auto chunk_todo = [&](int ch) -> bool {
+      // any block J in [64 ch, min(64 ch + 64, beta)) that is not selected
+      int j0 = ch * kChunk, j1 = min(j0 + kChunk, t.beta);
+      for (int J = j0; J < j1; J += 32) {
+        uint32_t wbits = selbits[J >> 5];
+        int n = min(32, j1 - J);
+        uint32_t mask = n == 32 ? 0xffffffffu : ((1u << n) - 1u);
+        if ((~wbits) & mask) return true;
+      }
+      return false;
+    };
+    auto next_step = [&](int it) -> int {
+      while (it < it1 && it >= T && !chunk_todo(it - T)) ++it;
+      return it;
+    };
+
+    // staging registers: K rows (4 x 8 elems), V quads (4 rows x 8 elems)
+    Vec8<DT> kst[4], vst[4];
+    const int krow0 = tid >> 4, kcol = (tid & 15) * 8;   // K: rows krow0 + 16 i, cols kcol..+8
+    const int vq = tid >> 4, vcol = (tid & 15) * 8;      // V: keys 4 vq..+4, cols vcol..+8
+    // the list must be strictly ascending; a split also checks the entry the
+    // previous split visited last
+    int prev_tile = 1 << 30;
+    if constexpr (!DENSE) {
+      if (it0 > 0 && it0 < T) prev_tile = idx[seg0 + T - it0];
+    }
+
+    auto load_step = [&](int it) {
+      if (it < T) {
+        int p;
+        if constexpr (DENSE) {
+          p = T - 1 - it;
+        } else {
+          p = idx[seg0 + T - 1 - it];
+          if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
+            if (tid == 0) atomicOr(&g.hdr->err, kErrIdx);
+            sh_bad = 1;
+            p = 0;
+          }
+          prev_tile = p;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int j = p * kTile + krow0 + 16 * i;
+          int64_t row = j < c.L ? kv_row(g, c, j) : -2;
+          if (row >= 0)
+            ld8<DT>(kst[i], (const char*)k + ((row * g.hkv + c.h) * kD + kcol) * C::EB);
+          else {
+            if (row == -1) { atomicOr(&g.hdr->err, kErrPage); sh_bad = 1; }
+            zero8<DT>(kst[i]);
+          }
+          int jv = p * kTile + 4 * vq + i;
+          int64_t rv = jv < c.L ? kv_row(g, c, jv) : -2;
+          if (rv >= 0)
+            ld8<DT>(vst[i], (const char*)v + ((rv * g.hkv + c.h) * kD + vcol) * C::EB);
+          else {
+            if (rv == -1) { atomicOr(&g.hdr->err, kErrPage); sh_bad = 1; }
+            zero8<DT>(vst[i]);
+          }
+        }
+      } else {
+        const int ch = it - T;
+        const int64_t mb = (int64_t)g.blk_base[c.b] + ch * kChunk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int J = ch * kChunk + krow0 + 16 * i;
+          if (J < t.beta)
+            ld8<DT>(kst[i], means + ml.kop + (((mb + krow0 + 16 * i) * g.hkv + c.h) * kD + kcol) * C::EB);
+          else
+            zero8<DT>(kst[i]);
+          int Jv = ch * kChunk + 4 * vq + i;
+          if (Jv < t.beta)
+            ld8<DT>(vst[i], means + ml.vop + (((mb + 4 * vq + i) * g.hkv + c.h) * kD + vcol) * C::EB);
+          else
+            zero8<DT>(vst[i]);
+        }
+      }
+    };
+
+    auto store_step = [&](int buf) {
+      char* ks = smem + buf * C::STAGE;
+      char* vt = ks + C::KBYTES;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        char* dst = ks + (krow0 + 16 * i) * C::KPITCH + kcol * C::EB;
+        if constexpr (DT == kBF16)
+          *(uint4*)dst = make_uint4(kst[i].w[0], kst[i].w[1], kst[i].w[2], kst[i].w[3]);
+        else if constexpr (DT == kE4M3)
+          *(uint2*)dst = make_uint2(kst[i].w[0], kst[i].w[1]);
+        else {
+          ((uint4*)dst)[0] = make_uint4(kst[i].w[0], kst[i].w[1], kst[i].w[2], kst[i].w[3]);
+          ((uint4*)dst)[1] = make_uint4(kst[i].w[4], kst[i].w[5], kst[i].w[6], kst[i].w[7]);
+        }
+      }
+      // V^T: column n gets keys 4vq..4vq+3 at their permuted positions
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        char* rowp = vt + (vcol + e) * C::VPITCH;
+        if constexpr (KPL >= 4) {
+          const int p0 = vt_pos<KPL>(4 * vq);
+          if constexpr (DT == kBF16) {
+            uint32_t lo = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 16);
+            uint32_t hi = el<DT>(vst[2], e) | (el<DT>(vst[3], e) << 16);
+            *(uint2*)(rowp + p0 * 2) = make_uint2(lo, hi);
+          } else {
+            uint32_t w = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 8) | (el<DT>(vst[2], e) << 16) |
+                         (el<DT>(vst[3], e) << 24);
+            *(uint32_t*)(rowp + p0) = w;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(uint32_t*)(rowp + vt_pos<KPL>(4 * vq + i) * 4) = el<DT>(vst[i], e);
+        }
+      }
+    };
+
+
+    // ---- mainloop
+    int cur = next_step(it0);
+    int buf = 0;
+    if (cur < it1) {
+      load_step(cur);
+      store_step(0);
+    }
+    __syncthreads();
+    int cur_tile = (cur < it1 && cur < T) ? prev_tile : -1;
+    if constexpr (DENSE) cur_tile = (cur < it1 && cur < T) ? T - 1 - cur : -1;
+    while (cur < it1) {
+      const int nxt = next_step(cur + 1);
+      if (nxt < it1) load_step(nxt);
+      int nxt_tile = (nxt < it1 && nxt < T) ? (DENSE ? T - 1 - nxt : prev_tile) : -1;
+
+      const char* ks = smem + buf * C::STAGE;
+      const char* vt = ks + C::KBYTES;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        sacc[jt] = f32x16{};
+        const char* arow = ks + (jt * 32 + col) * C::KPITCH + half * KPL * C::EB;
+#pragma unroll
+        for (int m = 0; m < C::NM0; ++m) {
+          Op a = lds_op<DT>(arow + m * 2 * KPL * C::EB);
+          sacc[jt] = mma<DT>(a, qf[m], sacc[jt]);
+        }
+      }
+      // scale, mask, row max
+      float mloc = -INFINITY;
+      if (cur < T) {
+        const int kbase = cur_tile * kTile;
+        const bool need_mask = kbase + kTile - 1 > t.t0;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = jt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            float x = sacc[jt][r] * sl;
+            if (need_mask && kbase + j > pos) x = -INFINITY;
+            sacc[jt][r] = x;
+            mloc = fmaxf(mloc, x);
+          }
+      } else {
+        const int j0 = (cur - T) * kChunk;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const int Jb = j0 + jt * 32 + 4 * half;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int J = Jb + 8 * (r >> 2) + (r & 3);
+            const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
+            // one mean stands for |B_J| = 128 tokens: + ln 128 = + 7 in log2 units
+            float x = ok ? sacc[jt][r] * sl + 7.f : -INFINITY;
+            sacc[jt][r] = x;
+            mloc = fmaxf(mloc, x);
+          }
+        }
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_i, mloc);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float resc = __builtin_amdgcn_exp2f(m_i - m_use);
+      m_i = m_new;
+      float psum = 0.f;
+      constexpr float kOff = DT == kE4M3 ? 8.f : 0.f;  // P scaled onto [0, 256] for e4m3
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(sacc[jt][r] - m_use + kOff);
+          sacc[jt][r] = p;
+        }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+
+      // P^T as B operands of O^T += V^T P^T
+      Op pf[C::NM1];
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int m1 = 0; m1 < 4; ++m1) {
+          bf16x8 b;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float pv = sacc[m1 >> 1][8 * (m1 & 1) + e];
+            psum += pv;
+            b[e] = static_cast<__bf16>(pv);
+          }
+          pf[m1] = b;
+        }
+      } else if constexpr (DT == kE4M3) {
+        i32x8 b;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int jt = w >> 2, r = (w & 3) * 4;
+          uint32_t lo = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]);
+          uint32_t hi = f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]);
+          uint32_t word = lo | (hi << 16);
+          f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P ([V2] Eq. 15)
+          psum += (back[0] + back[1]) + (back[2] + back[3]);
+          b[w] = (int)word;
+        }
+        pf[0] = b;
+      } else {
+#pragma unroll
+        for (int m1 = 0; m1 < 32; ++m1) {
+          float pv = sacc[m1 >> 4][m1 & 15];
+          psum += pv;
+          pf[m1] = pv;
+        }
+      }
+      l_i = l_i * resc + psum;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const char* arow = vt + (nt * 32 + col) * C::VPITCH + half * KPL * C::EB;
+#pragma unroll
+        for (int m1 = 0; m1 < C::NM1; ++m1) {
+          Op a = lds_op<DT>(arow + m1 * 2 * KPL * C::EB);
+          oacc[nt] = mma<DT>(a, pf[m1], oacc[nt]);
+        }
+      }
+      if (nxt < it1) store_step(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      cur = nxt;
+      cur_tile = nxt_tile;
+    }
+
+    // ---- epilogue
+    const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
+    const bool bad = sh_bad != 0;
+    if (un.nsplit == 1) {
+      if (row_ok) {
+        const float inv = (bad || !(l_tot > 0.f)) ? NAN : cvs / l_tot;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int n0 = nt * 32 + 8 * b4 + 4 * half;
+            float o0 = oacc[nt][4 * b4] * inv, o1 = oacc[nt][4 * b4 + 1] * inv;
+            float o2 = oacc[nt][4 * b4 + 2] * inv, o3 = oacc[nt][4 * b4 + 3] * inv;
+            if constexpr (DT == kF32) {
+              *(float4*)((float*)out + qrow * kD + n0) = make_float4(o0, o1, o2, o3);
+            } else {
+              uint32_t w0 = f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
+              uint32_t w1 = f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
+              *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(w0, w1);
+            }
+          }
+        if (lse && half == 0) {
+          constexpr float kOffL = DT == kE4M3 ? 8.f : 0.f;
+          lse[(c.row0 + pos) * g.hq + head] =
+              bad ? NAN : (m_i + __builtin_amdgcn_logf(l_tot) - kOffL) * 0.6931471805599453f;
+        }
+      }
+    } else {
+      // partial result of one split: O (unnormalised), m (log2), l
+      const int64_t slot = un.s * wl.umax + un.split;
+      float* po = (float*)(ws + wl.part_o) + slot * kRows * kD;
+      float* pml = (float*)(ws + wl.part_ml) + slot * 2 * kRows;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int n0 = nt * 32 + 8 * b4 + 4 * half;
+          float4 val = make_float4(oacc[nt][4 * b4], oacc[nt][4 * b4 + 1], oacc[nt][4 * b4 + 2],
+                                   oacc[nt][4 * b4 + 3]);
+          if (bad) val = make_float4(NAN, NAN, NAN, NAN);
+          *(float4*)(po + row_in_tile * kD + n0) = val;
+        }
+      if (half == 0) {
+        pml[row_in_tile] = m_i;
+        pml[kRows + row_in_tile] = bad ? NAN : l_tot;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Merge the splits of every split segment in split order (deterministic).
+template <int DT>
+__global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const char* __restrict__ ws,
+                                                      void* __restrict__ out, float* __restrict__ lse) {
+  const int64_t s = blockIdx.x;
+  const int32_t* nsplit = (const int32_t*)(ws + wl.counts);
+  const int U = nsplit[s];
+  if (U <= 1) return;
+  const SegCoord c = seg_coord(g, s);
+  const TileGeo t = tile_geo(g, c);
+  const int r = threadIdx.x >> 1, n0 = (threadIdx.x & 1) * 64;
+  if (r >= t.nrows) return;
+  const float* po = (const float*)(ws + wl.part_o);
+  const float* pml = (const float*)(ws + wl.part_ml);
+  float M = -INFINITY;
+  for (int u = 0; u < U; ++u) M = fmaxf(M, pml[(s * wl.umax + u) * 2 * kRows + r]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float wgt[16];
+  float L = 0.f;
+  for (int u = 0; u < U; ++u) {
+    const float* ml = pml + (s * wl.umax + u) * 2 * kRows;
+    wgt[u] = __builtin_amdgcn_exp2f(ml[r] - Mu);
+    L += wgt[u] * ml[kRows + r];
+  }
+  const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
+  const float inv = L > 0.f ? cvs / L : NAN;
+  const int64_t prow = c.I * kRows + r;
+  const int pos = (int)(prow >> g.log2g);
+  const int head = c.h * g.g + (int)(prow & (g.g - 1));
+  const int64_t qrow = (c.row0 + pos) * g.hq + head;
+  for (int n = n0; n < n0 + 64; n += 4) {
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < U; ++u) {
+      const float4 o = *(const float4*)(po + ((s * wl.umax + u) * kRows + r) * kD + n);
+      a[0] += wgt[u] * o.x;
+      a[1] += wgt[u] * o.y;
+      a[2] += wgt[u] * o.z;
+      a[3] += wgt[u] * o.w;
+    }
+    if constexpr (DT == kF32) {
+      *(float4*)((float*)out + qrow * kD + n) = make_float4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+    } else {
+      uint32_t w0 = f32_to_bf16_bits(a[0] * inv) | ((uint32_t)f32_to_bf16_bits(a[1] * inv) << 16);
+      uint32_t w1 = f32_to_bf16_bits(a[2] * inv) | ((uint32_t)f32_to_bf16_bits(a[3] * inv) << 16);
+      *(uint2*)((uint16_t*)out + qrow * kD + n) = make_uint2(w0, w1);
+    }
+  }
+  if (lse && n0 == 0) {
+    constexpr float kOffL = DT == kE4M3 ? 8.f : 0.f;
+    lse[(c.row0 + pos) * g.hq + head] = (Mu + __builtin_amdgcn_logf(L) - kOffL) * 0.6931471805599453f;
+  }
+}
+
+int attn_wgs_per_cu(int dtype) { return dtype == kF32 ? Cfg<kF32>::WGS : Cfg<kBF16>::WGS; }
+
+template <int DT, bool DENSE>
+static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
+                                const void* q, const void* k, const void* v, const int32_t* cu,
+                                const int32_t* idx, const char* means, int correction, void* out,
+                                float* lse, int grid, hipStream_t st) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<DT>::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  attn_kernel<DT, DENSE><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
+                                                           correction, out, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml, const void* q,
+                       const void* k, const void* v, const int32_t* cu, const int32_t* idx,
+                       const char* means, int dense, int correction, void* out, float* lse, int grid,
+                       hipStream_t st) {
+#define FP_ATTN(DT)                                                                                   \
+  return dense ? launch_attn_t<DT, true>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st) \
+               : launch_attn_t<DT, false>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse, \
+                                          grid, st)
+  switch (g.dtype) {
+    case kBF16: FP_ATTN(kBF16);
+    case kF32: FP_ATTN(kF32);
+    default: FP_ATTN(kE4M3);
+  }
+#undef FP_ATTN
+}
+
+hipError_t launch_combine(const Geo& g, const WsLayout& wl, char* ws, void* out, float* lse, hipStream_t st) {
+  dim3 grid((unsigned)g.n_seg);
+  switch (g.dtype) {
+    case kBF16: combine_kernel<kBF16><<<grid, 256, 0, st>>>(g, wl, ws, out, lse); break;
+    case kF32: combine_kernel<kF32><<<grid, 256, 0, st>>>(g, wl, ws, out, lse); break;
+    default: combine_kernel<kE4M3><<<grid, 256, 0, st>>>(g, wl, ws, out, lse); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp

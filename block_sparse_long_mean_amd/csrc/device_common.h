@@ -1,0 +1,123 @@
+// device_common.h -- small device helpers shared by the kernels of libfp.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp_internal.h"
+
+namespace fp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Two floats -> two OCP E4M3 codes packed in the low 16 bits (round to
+// nearest even; inputs are kept inside +-448 by the callers).
+__device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
+// Four E4M3 codes (one dword) -> four floats.
+__device__ __forceinline__ f32x4 e4m3x4_to_f32(uint32_t w) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f32x4 r;
+  r[0] = lo[0];
+  r[1] = lo[1];
+  r[2] = hi[0];
+  r[3] = hi[1];
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Segment s -> (request b, kv head h, tile I) through the per-request segment
+// offsets (binary search; segments are ordered request, kv head, tile).
+struct SegCoord {
+  int b, h;
+  int64_t I;
+  int L;        // request length
+  int64_t row0; // first Q row of the request
+};
+
+__device__ __forceinline__ SegCoord seg_coord(const Geo& g, int64_t s) {
+  int lo = 0, hi = g.nreq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)g.seg_off[mid] <= s)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  SegCoord c;
+  c.b = lo;
+  int64_t local = s - g.seg_off[lo];
+  int64_t nt = ((int64_t)g.seg_off[lo + 1] - g.seg_off[lo]) / g.hkv;
+  if (nt < 1) nt = 1;
+  c.h = (int)(local / nt);
+  c.I = local - (int64_t)c.h * nt;
+  c.row0 = g.cu_q[lo];
+  c.L = g.cu_q[lo + 1] - g.cu_q[lo];
+  return c;
+}
+
+// Tile geometry: valid packed rows, first/last position and the tile's block.
+struct TileGeo {
+  int nrows;
+  int t0, t1, beta;
+};
+
+__device__ __forceinline__ TileGeo tile_geo(const Geo& g, const SegCoord& c) {
+  TileGeo t;
+  int64_t packed = (int64_t)c.L << g.log2g;
+  int64_t r0 = c.I * kRows;
+  int64_t r1 = r0 + kRows;
+  if (r1 > packed) r1 = packed;
+  t.nrows = (int)(r1 - r0);
+  t.t0 = (int)(r0 >> g.log2g);
+  t.t1 = (int)((r1 - 1) >> g.log2g);
+  t.beta = t.t0 / kBlock;
+  return t;
+}
+
+// Row of the K/V storage holding token j of request b ([V2] Eq. 22), or -1
+// when the page table points outside the pool.
+__device__ __forceinline__ int64_t kv_row(const Geo& g, const SegCoord& c, int j) {
+  if (!g.page_table) return c.row0 + j;
+  int pg = j / g.page_size;
+  int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+  int64_t slot = page * g.page_size + (j - pg * g.page_size);
+  if (page < 0 || slot >= g.num_slots) return -1;
+  return slot;
+}
+
+__device__ __forceinline__ int elem_bytes(int dtype) {
+  return dtype == kF32 ? 4 : (dtype == kBF16 ? 2 : 1);
+}
+
+}  // namespace fp

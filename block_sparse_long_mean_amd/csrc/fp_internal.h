@@ -1,0 +1,97 @@
+// fp_internal.h -- types and launchers shared by the HIP translation units of
+// libfp.so.  Nothing here is part of the public ABI (include/fp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp {
+
+// Fixed geometry of the method ([V2] §3.3 implementation details, §4.1):
+// head dimension 128, selection block 128 tokens, physical key tile 64 tokens,
+// query tile 128 packed rows.
+constexpr int kD = 128;
+constexpr int kBlock = 128;
+constexpr int kTile = 64;
+constexpr int kRows = 128;
+constexpr int kChunk = 64;        // blocks per correction chunk / padding unit of the means
+constexpr int kMaxBlocks = 8192;  // longest request: 8192 blocks = 1,048,576 tokens
+constexpr int kBuckets = 4096;    // work-size buckets of the scheduler
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+
+// Device error flag bits (workspace header word 0).
+constexpr int32_t kErrPage = 1;
+constexpr int32_t kErrIdx = 2;
+
+// Workspace header words.
+struct WsHeader {
+  int32_t err;
+  int32_t work_counter;
+  int32_t total_units;
+  int32_t pad[61];
+};
+
+// Everything a kernel needs to walk the batch.  Passed by value.
+struct Geo {
+  const int32_t* cu_q;        // [nreq+1]
+  const int32_t* page_table;  // nullable
+  int64_t num_slots;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t nreq, hq, hkv, g, log2g;
+  int32_t dtype;
+  const float* descale;       // [3] for E4M3
+  float scale;                // sigma
+  int32_t max_nj;             // largest candidate-block count of a segment
+  int32_t words;              // selection bitmask words per segment
+  int64_t n_seg;
+  int64_t nb_pad;             // padded block count of the means arrays
+  // workspace views
+  WsHeader* hdr;
+  int32_t* seg_off;           // [nreq+1] first segment of each request
+  int32_t* blk_base;          // [nreq+1] first (padded) block of each request
+};
+
+// Layout of the pooled-statistics buffer (byte offsets).
+struct MeansLayout {
+  size_t kbar32, vbar32;  // float [nb_pad][hkv][128]
+  size_t khi, klo;        // bf16, MFMA B-operand order: [nb_pad/32][hkv][8][64][8]
+  size_t kop, vop;        // element dtype, [nb_pad][hkv][128]: operands of correction steps
+  size_t total;
+};
+
+// Layout of the workspace (byte offsets).
+struct WsLayout {
+  size_t hdr, seg_off, blk_base, counts, bits, hist, cursor, units, part_o, part_ml, total;
+  int32_t umax;           // largest split count of one segment
+};
+
+struct SplitPolicy {
+  int32_t umax;
+  int32_t min_split;      // fewest iterations a split unit gets
+};
+
+// --- launchers (each returns hipSuccess or the launch error) ---
+hipError_t launch_meta(const Geo& g, hipStream_t st);
+hipError_t launch_pool(const Geo& g, const MeansLayout& ml, const void* k, const void* v,
+                       char* means, hipStream_t st);
+hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* q,
+                               const char* means, float alpha, int sink, int win,
+                               int32_t* counts, uint32_t* bits, float* energies, hipStream_t st);
+hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, hipStream_t st);
+hipError_t launch_expand(const Geo& g, const int32_t* cu, const uint32_t* bits, int32_t* idx,
+                         int64_t cap, hipStream_t st);
+hipError_t launch_sched(const Geo& g, const WsLayout& wl, char* ws, const int32_t* cu,
+                        int dense, int correction, const SplitPolicy& sp, hipStream_t st);
+hipError_t launch_attn(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
+                       const void* q, const void* k, const void* v, const int32_t* cu,
+                       const int32_t* idx, const char* means, int dense, int correction,
+                       void* out, float* lse, int grid, hipStream_t st);
+hipError_t launch_combine(const Geo& g, const WsLayout& wl, char* ws, void* out, float* lse,
+                          hipStream_t st);
+
+int attn_wgs_per_cu(int dtype);
+
+}  // namespace fp

@@ -1,0 +1,312 @@
+// select.hip -- index stage after pooling: block scoring, alpha*max selection,
+// CSR offsets and CSR expansion.
+//
+// Scoring ([V2] §3.1 Eq. 1-3, §3.3 Eq. 19-20).  One workgroup per segment
+// (one PackGQA query tile of 128 packed rows of one KV head).  The tile's Q
+// rows are staged once in LDS; every wave takes 32-block column tiles of the
+// pooled keys and computes the 128x32 logit tile with bf16 MFMAs.  kbar is
+// fp32, split into bf16 hi + lo (two MFMAs per step, ~16 significant bits)
+// so that the normalised energies are accurate to ~1e-5 relative; fp32
+// queries are split the same way (three MFMAs).  Each lane owns one block
+// column and 64 of its 128 rows, so the per-block maximum m_J and the energy
+// S_J = sum_r 2^(s_rJ log2 e - m_J) (the form of Eq. 1, in log2 units) need
+// only one cross-lane exchange and no workgroup barrier; the final rescale
+// E_J = S_J 2^(m_J - M) with M = max_J m_J is the step Eq. 20 describes.
+// Selection keeps E_J >= alpha * max E or forced blocks, writes one bit per
+// block and the segment's tile count; no energy array goes to HBM.
+#include "device_common.h"
+
+namespace fp {
+
+constexpr int kQPitch = kD + 8;  // bf16 elements per staged Q row (bank spread)
+
+__device__ __forceinline__ float block_max(float x, float* red) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// Stage the tile's 128 packed query rows as bf16 (hi, and lo for fp32 input).
+template <int DT>
+__device__ __forceinline__ void stage_q(const Geo& g, const SegCoord& c, const TileGeo& t,
+                                        const void* q, uint16_t* qh, uint16_t* ql) {
+  const int tid = threadIdx.x;
+  const int64_t r0 = c.I * kRows;
+  if constexpr (DT == kBF16) {
+    for (int i = tid; i < kRows * 16; i += 256) {
+      int r = i >> 4, ch = i & 15;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (r < t.nrows) {
+        int64_t pr = r0 + r;
+        int64_t row = c.row0 + (pr >> g.log2g);
+        int head = c.h * g.g + (int)(pr & (g.g - 1));
+        w = *(const uint4*)((const uint16_t*)q + (row * g.hq + head) * kD + ch * 8);
+      }
+      *(uint4*)(qh + r * kQPitch + ch * 8) = w;
+    }
+  } else if constexpr (DT == kE4M3) {
+    for (int i = tid; i < kRows * 8; i += 256) {
+      int r = i >> 3, ch = i & 7;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (r < t.nrows) {
+        int64_t pr = r0 + r;
+        int64_t row = c.row0 + (pr >> g.log2g);
+        int head = c.h * g.g + (int)(pr & (g.g - 1));
+        w = *(const uint4*)((const uint8_t*)q + (row * g.hq + head) * kD + ch * 16);
+      }
+      uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+      uint16_t o[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 f = e4m3x4_to_f32(ww[j]);  // exact in bf16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[4 * j + e] = f32_to_bf16_bits(f[e]);
+      }
+      uint4* dst = (uint4*)(qh + r * kQPitch + ch * 16);
+      dst[0] = *(uint4*)&o[0];
+      dst[1] = *(uint4*)&o[8];
+    }
+  } else {
+    for (int i = tid; i < kRows * 32; i += 256) {
+      int r = i >> 5, ch = i & 31;
+      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < t.nrows) {
+        int64_t pr = r0 + r;
+        int64_t row = c.row0 + (pr >> g.log2g);
+        int head = c.h * g.g + (int)(pr & (g.g - 1));
+        w = *(const float4*)((const float*)q + (row * g.hq + head) * kD + ch * 4);
+      }
+      float f[4] = {w.x, w.y, w.z, w.w};
+      uint16_t oh[4], ol[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oh[e] = f32_to_bf16_bits(f[e]);
+        ol[e] = f32_to_bf16_bits(f[e] - bf16_bits_to_f32(oh[e]));
+      }
+      *(uint2*)(qh + r * kQPitch + ch * 4) = *(uint2*)oh;
+      *(uint2*)(ql + r * kQPitch + ch * 4) = *(uint2*)ol;
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml, const void* __restrict__ q,
+                                                           const char* __restrict__ means, float alpha,
+                                                           int sink, int win, int32_t* __restrict__ counts,
+                                                           uint32_t* __restrict__ bits,
+                                                           float* __restrict__ energies) {
+  extern __shared__ __align__(16) char smem[];
+  constexpr int NQ = DT == kF32 ? 2 : 1;
+  uint16_t* qh = (uint16_t*)smem;
+  uint16_t* ql = qh + kRows * kQPitch;
+  float* mJ = (float*)(smem + NQ * kRows * kQPitch * 2);
+  float* SJ = mJ + g.max_nj;
+  __shared__ float red[4];
+  __shared__ int nsel_w[4];
+
+  const int64_t s = blockIdx.x;
+  const SegCoord c = seg_coord(g, s);
+  const TileGeo t = tile_geo(g, c);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  stage_q<DT>(g, c, t, q, qh, ql);
+  __syncthreads();
+
+  const float sl = g.scale * 1.4426950408889634f * (DT == kE4M3 ? g.descale[0] : 1.f);
+  const int nc = t.beta + 1;
+  const int njt = (nc + 31) >> 5;
+  const bf16x8* khi = (const bf16x8*)(means + ml.khi);
+  const bf16x8* klo = (const bf16x8*)(means + ml.klo);
+  const int64_t jt0 = g.blk_base[c.b] >> 5;
+  const int half = lane >> 5, col = lane & 31;
+
+  for (int jt = wave; jt < njt; jt += 4) {
+    const int64_t fb = (((jt0 + jt) * g.hkv + c.h) * 8) * 64 + lane;
+    bf16x8 bh[8], bl[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bh[ks] = khi[fb + ks * 64];
+      bl[ks] = klo[fb + ks * 64];
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      acc[rt] = f32x16{};
+      const uint16_t* arow = qh + (rt * 32 + col) * kQPitch + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 a = *(const bf16x8*)(arow + ks * 16);
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc[rt], 0, 0, 0);
+        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc[rt], 0, 0, 0);
+        if constexpr (NQ == 2) {
+          bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
+          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc[rt], 0, 0, 0);
+        }
+      }
+    }
+    // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int row = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        float x = row < t.nrows ? acc[rt][r] * sl : -INFINITY;
+        acc[rt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[rt][r] - mx);
+    sum += __shfl_xor(sum, 32, 64);
+    const int J = jt * 32 + col;
+    if (half == 0 && J < nc) {
+      mJ[J] = mx;
+      SJ[J] = sum;
+    }
+  }
+  __syncthreads();
+
+  // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced.
+  float lm = -INFINITY;
+  for (int J = threadIdx.x; J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
+  const float M = block_max(lm, red);
+  float le = 0.f;
+  for (int J = threadIdx.x; J < nc; J += 256) {
+    float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
+    SJ[J] = e;
+    le = fmaxf(le, e);
+  }
+  const float Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
+  const float thr = alpha * Emax;
+  int nsel = 0;
+  for (int base = wave * 64; base < nc; base += 256) {
+    const int J = base + lane;
+    const bool in = J < nc;
+    const bool forced = J < sink || (J >= t.beta - win && J < t.beta) || J == t.beta;
+    const bool sel = in && (forced || SJ[J] >= thr);
+    const uint64_t m = __ballot(sel);
+    if (lane == 0) {
+      int w0 = base >> 5;
+      bits[s * g.words + w0] = (uint32_t)m;
+      if (w0 + 1 < g.words) bits[s * g.words + w0 + 1] = (uint32_t)(m >> 32);
+    }
+    nsel += __popcll(m);
+    if (energies && in) energies[s * g.max_nj + J] = SJ[J] / Emax;
+  }
+  if (energies)
+    for (int J = nc + threadIdx.x; J < g.max_nj; J += 256) energies[s * g.max_nj + J] = -1.f;
+  if (lane == 0) nsel_w[wave] = nsel;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = nsel_w[0] + nsel_w[1] + nsel_w[2] + nsel_w[3];
+    // each kept block gives tiles 2J and 2J+1; the diagonal block's second tile
+    // is dropped when it starts after the tile's last position
+    int trim = (int64_t)kTile * (2 * t.beta + 1) > t.t1 ? 1 : 0;
+    counts[s] = 2 * tot - trim;
+  }
+}
+
+// Exclusive prefix sum of the per-segment counts into cu[n+1] (one workgroup).
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int64_t n,
+                                                   int32_t* __restrict__ cu) {
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = tid * per, hi = min(lo + per, n);
+  int64_t loc = 0;
+  for (int64_t i = lo; i < hi; ++i) loc += counts[i];
+  part[tid] = loc;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int64_t a = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += a;
+    __syncthreads();
+  }
+  int64_t run = part[tid] - loc;
+  for (int64_t i = lo; i < hi; ++i) {
+    cu[i] = (int32_t)run;
+    run += counts[i];
+  }
+  if (tid == 1023) cu[n] = (int32_t)part[1023];
+}
+
+// One wave per segment: ballot + prefix count turn the selection bits into the
+// ascending list of physical tile ids (logical block J -> tiles 2J, 2J+1).
+__global__ __launch_bounds__(256) void expand_kernel(Geo g, const int32_t* __restrict__ cu,
+                                                     const uint32_t* __restrict__ bits,
+                                                     int32_t* __restrict__ idx, int64_t cap) {
+  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (s >= g.n_seg) return;
+  const int lane = threadIdx.x & 63;
+  const SegCoord c = seg_coord(g, s);
+  const TileGeo t = tile_geo(g, c);
+  const int64_t start = cu[s];
+  const int nc = t.beta + 1;
+  int o = 0;
+  for (int base = 0; base < nc; base += 64) {
+    const int J = base + lane;
+    bool sel = false;
+    if (J < nc) sel = (bits[s * g.words + (J >> 5)] >> (J & 31)) & 1u;
+    const uint64_t m = __ballot(sel);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (sel) {
+      int64_t pos = start + o + 2 * before;
+      if (pos < cap) idx[pos] = 2 * J;
+      if ((int64_t)kTile * (2 * J + 1) <= t.t1 && pos + 1 < cap) idx[pos + 1] = 2 * J + 1;
+    }
+    o += 2 * __popcll(m);
+  }
+}
+
+hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* q, const char* means,
+                               float alpha, int sink, int win, int32_t* counts, uint32_t* bits,
+                               float* energies, hipStream_t st) {
+  const int nq = g.dtype == kF32 ? 2 : 1;
+  size_t lds = (size_t)nq * kRows * kQPitch * 2 + (size_t)g.max_nj * 8;
+  dim3 grid((unsigned)g.n_seg);
+  static bool attr_set[3] = {false, false, false};
+  if (!attr_set[g.dtype]) {
+    const void* fn = g.dtype == kBF16 ? (const void*)score_select_kernel<kBF16>
+                     : g.dtype == kF32 ? (const void*)score_select_kernel<kF32>
+                                       : (const void*)score_select_kernel<kE4M3>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       2 * kRows * kQPitch * 2 + kMaxBlocks * 8);
+    if (e != hipSuccess) return e;
+    attr_set[g.dtype] = true;
+  }
+  switch (g.dtype) {
+    case kBF16:
+      score_select_kernel<kBF16><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
+                                                         energies);
+      break;
+    case kF32:
+      score_select_kernel<kF32><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
+                                                        energies);
+      break;
+    default:
+      score_select_kernel<kE4M3><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
+                                                         energies);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, hipStream_t st) {
+  scan_kernel<<<1, 1024, 0, st>>>(counts, n, cu);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const Geo& g, const int32_t* cu, const uint32_t* bits, int32_t* idx, int64_t cap,
+                         hipStream_t st) {
+  expand_kernel<<<(unsigned)((g.n_seg + 3) / 4), 256, 0, st>>>(g, cu, bits, idx, cap);
+  return hipGetLastError();
+}
+
+}  // namespace fp

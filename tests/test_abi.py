@@ -1,0 +1,154 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry
+point, and rejects bad host arguments before launching anything."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp.h")
+
+
+def _fp():
+    from block_sparse_long_mean_amd import fp
+    return fp
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["fp_query_sizes", "fp_pool", "fp_select", "fp_sparse_attn", "fp_dense_attn",
+              "fp_read_device_error", "fp_status_string", "fp_last_error", "fp_block_base"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    fp = _fp()
+    lib = fp.lib_handle()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def _problem(fp, lengths=(1000, 300), hq=32, hkv=4, dtype=1, **kw):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    p = fp.Problem()
+    p.num_reqs = len(lengths)
+    p.num_heads_q = hq
+    p.num_heads_kv = hkv
+    p.head_dim = kw.get("head_dim", 128)
+    p.cu_seqlens_q = 0x1000  # never dereferenced on the host
+    p.cu_seqlens_q_host = cu.ctypes.data
+    p.page_table = kw.get("page_table", None)
+    p.page_size = kw.get("page_size", 0)
+    p.max_pages_per_req = kw.get("max_pages", 0)
+    p.num_pool_slots = kw.get("slots", 0)
+    p.dtype = dtype
+    p.descale = kw.get("descale", None)
+    p.softmax_scale = kw.get("scale", 0.0)
+    return p, cu
+
+
+def _sizes(fp, p, params=None):
+    out = fp.Sizes()
+    st = fp.lib_handle().fp_query_sizes(C.byref(p), C.byref(params) if params else None, C.byref(out))
+    return st, out
+
+
+def test_query_sizes_geometry():
+    fp = _fp()
+    p, cu = _problem(fp, lengths=(1000, 300))
+    st, s = _sizes(fp, p, fp.select_params())
+    assert st == 0
+    g = 8
+    nseg = 4 * (math.ceil(g * 1000 / 128) + math.ceil(g * 300 / 128))
+    assert s.n_segments == nseg
+    assert s.max_blocks == 8
+    # worst-case CSR: every causal 64-token tile of every segment
+    cap = 0
+    for L in (1000, 300):
+        for I in range(math.ceil(g * L / 128)):
+            t1 = (min((I + 1) * 128, g * L) - 1) // g
+            cap += 4 * (t1 // 64 + 1)
+    assert s.idx_capacity == cap
+    assert s.means_bytes > 0 and s.workspace_bytes > 0
+    assert fp.lib_handle().fp_block_base(C.byref(p), 1) == 64
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, -2),
+    ("num_heads_q", 30, -1),
+    ("num_heads_q", 4 * 3, -2),
+    ("dtype", 7, -1),
+    ("num_reqs", 0, -1),
+    ("softmax_scale", float("nan"), -1),
+])
+def test_invalid_problems_are_rejected(field, value, code):
+    fp = _fp()
+    p, cu = _problem(fp)
+    setattr(p, field, value)
+    st, _ = _sizes(fp, p)
+    assert st == code, fp.lib_handle().fp_last_error()
+    assert fp.lib_handle().fp_last_error()
+
+
+def test_decreasing_offsets_and_missing_descale_are_rejected():
+    fp = _fp()
+    p, cu = _problem(fp, lengths=(100, 200))
+    cu[2] = 50
+    assert _sizes(fp, p)[0] == -1
+    p, cu = _problem(fp, dtype=2)
+    assert _sizes(fp, p)[0] == -1
+    p, cu = _problem(fp, lengths=(1 << 21,))
+    assert _sizes(fp, p)[0] == -2
+
+
+def test_paged_arguments_are_checked():
+    fp = _fp()
+    pt = np.zeros((2, 4), np.int32)
+    p, cu = _problem(fp, lengths=(1000, 300), page_table=pt.ctypes.data, page_size=64, max_pages=4, slots=1 << 20)
+    assert _sizes(fp, p)[0] == -1  # 4 pages of 64 cannot hold 1000 tokens
+    p.max_pages_per_req = 16
+    assert _sizes(fp, p)[0] == 0
+    p.page_size = 0
+    assert _sizes(fp, p)[0] == -1
+
+
+@pytest.mark.parametrize("alpha,block,sink,code", [(float("nan"), 128, 2, -1), (-0.1, 128, 2, -1),
+                                                    (0.1, 64, 2, -2), (0.1, 128, -1, -1)])
+def test_invalid_select_params(alpha, block, sink, code):
+    fp = _fp()
+    p, cu = _problem(fp)
+    sp = fp.SelectParams(alpha, block, sink, 4)
+    assert _sizes(fp, p, sp)[0] == code
+
+
+def test_calls_fail_before_launch_on_small_buffers():
+    fp = _fp()
+    lib = fp.lib_handle()
+    p, cu = _problem(fp)
+    sp = fp.select_params()
+    st, s = _sizes(fp, p, sp)
+    dummy = C.c_void_p(0x1000)
+    # workspace too small
+    r = lib.fp_select(C.byref(p), C.byref(sp), dummy, dummy, dummy, dummy, dummy, s.idx_capacity, dummy, None,
+                      dummy, s.workspace_bytes - 1, None)
+    assert r == -3
+    # idx capacity too small
+    r = lib.fp_select(C.byref(p), C.byref(sp), dummy, dummy, dummy, dummy, dummy, s.idx_capacity - 1, dummy,
+                      None, dummy, s.workspace_bytes, None)
+    assert r == -4
+    # missing tensors
+    r = lib.fp_sparse_attn(C.byref(p), C.byref(sp), None, dummy, dummy, dummy, dummy, dummy, 1, dummy, None,
+                           dummy, s.workspace_bytes, None)
+    assert r == -1
+    r = lib.fp_dense_attn(C.byref(p), dummy, dummy, dummy, dummy, None, None, s.workspace_bytes, None)
+    assert r == -1
+    assert lib.fp_status_string(-3) == b"workspace too small"
