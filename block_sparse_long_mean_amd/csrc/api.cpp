@@ -157,6 +157,7 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
   w.seg_off = o; o = align256(o + (size_t)(p->num_reqs + 1) * 4);
   w.blk_base = o; o = align256(o + (size_t)(p->num_reqs + 1) * 4);
   w.counts = o; o = align256(o + (size_t)hg.n_seg * 4);
+  w.scan_part = o; o = align256(o + (size_t)((hg.n_seg + 1023) / 1024 + 1) * 4);
   w.bits = o; o = align256(o + (size_t)hg.n_seg * hg.words * 4);
   w.hist = o; o = align256(o + (size_t)kBuckets * 4);
   w.cursor = o; o = align256(o + (size_t)kBuckets * 4);
@@ -297,7 +298,7 @@ fp_status fp_select(const fp_problem* prob, const fp_select_params* params, cons
   FP_LAUNCH(launch_pool(pr.g, pr.ml, k, v, (char*)means, st));
   FP_LAUNCH(launch_score_select(pr.g, pr.ml, q, (const char*)means, params->alpha, params->sink_blocks,
                                 params->window_blocks, counts, bits, energies, st));
-  FP_LAUNCH(launch_scan(counts, pr.hg.n_seg, cu, st));
+  FP_LAUNCH(launch_scan(counts, pr.hg.n_seg, cu, (int32_t*)(wsb + pr.wl.scan_part), st));
   FP_LAUNCH(launch_expand(pr.g, cu, bits, idx, idx_capacity, st));
   return FP_OK;
 }

@@ -147,7 +147,24 @@ struct Unit {
   int split, nsplit;
 };
 
-template <int DT, bool DENSE>
+// Offset (in head vectors, i.e. row * hkv + h) of token j of the segment's
+// request.  PAGED: through the page table ([V2] Eq. 22); an entry outside
+// the pool sets kErrPage in err and reads row 0 instead.
+template <bool PAGED>
+__device__ __forceinline__ int64_t tok_vec(const Geo& g, const SegCoord& c, int j, uint32_t& err) {
+  if constexpr (!PAGED) {
+    return (c.row0 + j) * g.hkv + c.h;
+  } else {
+    const int pg = j / g.page_size;
+    const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+    const int64_t slot = page * g.page_size + (j - pg * g.page_size);
+    const bool ok = page >= 0 && slot < g.num_slots;
+    err |= ok ? 0u : (uint32_t)kErrPage;
+    return (ok ? slot : 0) * g.hkv + c.h;
+  }
+}
+
+template <int DT, bool DENSE, bool PAGED>
 __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     Geo g, WsLayout wl, char* __restrict__ ws, MeansLayout ml, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ cu,
@@ -156,31 +173,36 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   using C = Cfg<DT>;
   using Op = typename Tr<DT>::Op;
   constexpr int KPL = C::KPL;
+  constexpr int EB = C::EB;
   extern __shared__ __align__(16) char smem[];
   uint32_t* selbits = (uint32_t*)(smem + 2 * C::STAGE);
   __shared__ int sh_unit;
-  __shared__ int sh_bad;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int2* units = (const int2*)(ws + wl.units);
+  // logits in log2 units: x = s * sl (+ 7 for a mean that stands for 128 keys)
   const float sl = g.scale * 1.4426950408889634f *
                    (DT == kE4M3 ? g.descale[0] * g.descale[1] : 1.f);
   const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
+  constexpr float kOff = DT == kE4M3 ? 8.f : 0.f;  // e4m3: P scaled onto [0, 256] (Eq. 15)
+
+  // staging assignment: K rows kr + 16 i, columns kc..kc+7 (16 lanes per row);
+  // V key quad vq (keys 4vq..4vq+3), columns vc..vc+7 (16 lanes per V^T row)
+  const int kr = tid >> 4, kc = (tid & 15) * 8;
+  const int vq = tid & 15, vc = (tid >> 4) * 8;
+  const int vpos = vt_pos<KPL>(4 * vq);
 
   for (;;) {
-    if (tid == 0) {
-      int u = atomicAdd(&g.hdr->work_counter, 1);
-      sh_unit = u;
-      sh_bad = 0;
-    }
+    if (tid == 0) sh_unit = atomicAdd(&g.hdr->work_counter, 1);
     __syncthreads();
     const int u = sh_unit;
     if (u >= g.hdr->total_units) break;
     const int2 ud = units[u];
-    Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
+    const Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
     const SegCoord c = seg_coord(g, un.s);
     const TileGeo t = tile_geo(g, c);
+    uint32_t err = 0;
     int T, seg0 = 0;
     if constexpr (DENSE) {
       T = t.t1 / kTile + 1;
@@ -188,7 +210,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       seg0 = cu[un.s];
       T = cu[un.s + 1] - seg0;
       if (T < 0 || T > 2 * (t.beta + 1)) {
-        if (tid == 0) { atomicOr(&g.hdr->err, kErrIdx); sh_bad = 1; }
+        err |= kErrIdx;
         T = 0;
       }
     }
@@ -201,14 +223,13 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       for (int w = tid; w <= (t.beta >> 5); w += 256) selbits[w] = 0;
       __syncthreads();
       for (int e = tid; e < T; e += 256) {
-        int p = idx[seg0 + e];
-        int J = p / 2;
+        const int J = idx[seg0 + e] >> 1;
         if (J >= 0 && J < t.beta) atomicOr(&selbits[J >> 5], 1u << (J & 31));
       }
     }
     __syncthreads();
 
-    // ---- the wave's 32 query rows as the B operand of S^T = K Q^T
+    // ---- the wave's 32 query rows: B operand of S^T = K Q^T, kept in registers
     const int row_in_tile = wave * 32 + col;
     const bool row_ok = row_in_tile < t.nrows;
     const int64_t prow = c.I * kRows + row_in_tile;
@@ -219,20 +240,20 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
     for (int m = 0; m < C::NM0; ++m) {
       const int d0 = m * 2 * KPL + half * KPL;
+      const char* src = (const char*)q + (qrow * kD + d0) * EB;
       if constexpr (DT == kBF16) {
-        uint4 w = row_ok ? *(const uint4*)((const uint16_t*)q + qrow * kD + d0) : make_uint4(0, 0, 0, 0);
+        uint4 w = row_ok ? *(const uint4*)src : make_uint4(0, 0, 0, 0);
         qf[m] = __builtin_bit_cast(bf16x8, w);
       } else if constexpr (DT == kE4M3) {
         i32x8 w = {};
         if (row_ok) {
-          const uint4* p = (const uint4*)((const uint8_t*)q + qrow * kD + d0);
-          uint4 a = p[0], b = p[1];
+          uint4 a = ((const uint4*)src)[0], b = ((const uint4*)src)[1];
           w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
           w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
         }
         qf[m] = w;
       } else {
-        qf[m] = row_ok ? ((const float*)q)[qrow * kD + d0] : 0.f;
+        qf[m] = row_ok ? *(const float*)src : 0.f;
       }
     }
 
@@ -241,15 +262,13 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) oacc[nt] = f32x16{};
 
-    // ---- step descriptors: tiles (backwards through the list), then chunks
+    // ---- steps: listed tiles backwards (Eq. 17), then correction chunks
     auto chunk_todo = [&](int ch) -> bool {
-      // any block J in [64 ch, min(64 ch + 64, beta)) that is not selected
-      int j0 = ch * kChunk, j1 = min(j0 + kChunk, t.beta);
+      const int j0 = ch * kChunk, j1 = min(j0 + kChunk, t.beta);
       for (int J = j0; J < j1; J += 32) {
-        uint32_t wbits = selbits[J >> 5];
-        int n = min(32, j1 - J);
-        uint32_t mask = n == 32 ? 0xffffffffu : ((1u << n) - 1u);
-        if ((~wbits) & mask) return true;
+        const int n = min(32, j1 - J);
+        const uint32_t mask = n == 32 ? 0xffffffffu : ((1u << n) - 1u);
+        if ((~selbits[J >> 5]) & mask) return true;
       }
       return false;
     };
@@ -257,66 +276,49 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       while (it < it1 && it >= T && !chunk_todo(it - T)) ++it;
       return it;
     };
-
-    // staging registers: K rows (4 x 8 elems), V quads (4 rows x 8 elems)
-    Vec8<DT> kst[4], vst[4];
-    const int krow0 = tid >> 4, kcol = (tid & 15) * 8;   // K: rows krow0 + 16 i, cols kcol..+8
-    const int vq = tid >> 4, vcol = (tid & 15) * 8;      // V: keys 4 vq..+4, cols vcol..+8
-    // the list must be strictly ascending; a split also checks the entry the
-    // previous split visited last
+    // strictly ascending list: a split also checks the entry its predecessor saw last
     int prev_tile = 1 << 30;
     if constexpr (!DENSE) {
       if (it0 > 0 && it0 < T) prev_tile = idx[seg0 + T - it0];
     }
-
-    auto load_step = [&](int it) {
-      if (it < T) {
-        int p;
-        if constexpr (DENSE) {
-          p = T - 1 - it;
-        } else {
-          p = idx[seg0 + T - 1 - it];
-          if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
-            if (tid == 0) atomicOr(&g.hdr->err, kErrIdx);
-            sh_bad = 1;
-            p = 0;
-          }
-          prev_tile = p;
+    auto tile_of = [&](int it) -> int {
+      if constexpr (DENSE) {
+        return T - 1 - it;
+      } else {
+        int p = idx[seg0 + T - 1 - it];
+        if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
+          err |= kErrIdx;
+          p = 0;
         }
+        prev_tile = p;
+        return p;
+      }
+    };
+
+    Vec8<DT> kst[4], vst[4];
+    auto load_step = [&](int it, int p) {
+      if (it < T) {
+        const char* kb = (const char*)k + (int64_t)kc * EB;
+        const char* vb = (const char*)v + (int64_t)vc * EB;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int j = p * kTile + krow0 + 16 * i;
-          int64_t row = j < c.L ? kv_row(g, c, j) : -2;
-          if (row >= 0)
-            ld8<DT>(kst[i], (const char*)k + ((row * g.hkv + c.h) * kD + kcol) * C::EB);
-          else {
-            if (row == -1) { atomicOr(&g.hdr->err, kErrPage); sh_bad = 1; }
-            zero8<DT>(kst[i]);
-          }
-          int jv = p * kTile + 4 * vq + i;
-          int64_t rv = jv < c.L ? kv_row(g, c, jv) : -2;
-          if (rv >= 0)
-            ld8<DT>(vst[i], (const char*)v + ((rv * g.hkv + c.h) * kD + vcol) * C::EB);
-          else {
-            if (rv == -1) { atomicOr(&g.hdr->err, kErrPage); sh_bad = 1; }
-            zero8<DT>(vst[i]);
-          }
+          // tokens past the end of the request are causally masked for every
+          // row; reading the last token keeps V finite
+          const int jk = min(p * kTile + kr + 16 * i, c.L - 1);
+          const int jv = min(p * kTile + 4 * vq + i, c.L - 1);
+          ld8<DT>(kst[i], kb + tok_vec<PAGED>(g, c, jk, err) * (kD * EB));
+          ld8<DT>(vst[i], vb + tok_vec<PAGED>(g, c, jv, err) * (kD * EB));
         }
       } else {
-        const int ch = it - T;
-        const int64_t mb = (int64_t)g.blk_base[c.b] + ch * kChunk;
+        // pooled means of blocks 64 ch .. 64 ch + 63 (the padded arrays hold
+        // zeros past the request's last block)
+        const int64_t mb = ((int64_t)g.blk_base[c.b] + (it - T) * kChunk) * g.hkv + c.h;
+        const char* kb = means + ml.kop + (int64_t)kc * EB;
+        const char* vb = means + ml.vop + (int64_t)vc * EB;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int J = ch * kChunk + krow0 + 16 * i;
-          if (J < t.beta)
-            ld8<DT>(kst[i], means + ml.kop + (((mb + krow0 + 16 * i) * g.hkv + c.h) * kD + kcol) * C::EB);
-          else
-            zero8<DT>(kst[i]);
-          int Jv = ch * kChunk + 4 * vq + i;
-          if (Jv < t.beta)
-            ld8<DT>(vst[i], means + ml.vop + (((mb + 4 * vq + i) * g.hkv + c.h) * kD + vcol) * C::EB);
-          else
-            zero8<DT>(vst[i]);
+          ld8<DT>(kst[i], kb + (mb + (int64_t)(kr + 16 * i) * g.hkv) * (kD * EB));
+          ld8<DT>(vst[i], vb + (mb + (int64_t)(4 * vq + i) * g.hkv) * (kD * EB));
         }
       }
     };
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       char* vt = ks + C::KBYTES;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        char* dst = ks + (krow0 + 16 * i) * C::KPITCH + kcol * C::EB;
+        char* dst = ks + (kr + 16 * i) * C::KPITCH + kc * EB;
         if constexpr (DT == kBF16)
           *(uint4*)dst = make_uint4(kst[i].w[0], kst[i].w[1], kst[i].w[2], kst[i].w[3]);
         else if constexpr (DT == kE4M3)
@@ -336,21 +338,17 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           ((uint4*)dst)[1] = make_uint4(kst[i].w[4], kst[i].w[5], kst[i].w[6], kst[i].w[7]);
         }
       }
-      // V^T: column n gets keys 4vq..4vq+3 at their permuted positions
+      // V^T: row n = vc + e receives keys 4vq..4vq+3 at their permuted position
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        char* rowp = vt + (vcol + e) * C::VPITCH;
-        if constexpr (KPL >= 4) {
-          const int p0 = vt_pos<KPL>(4 * vq);
-          if constexpr (DT == kBF16) {
-            uint32_t lo = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 16);
-            uint32_t hi = el<DT>(vst[2], e) | (el<DT>(vst[3], e) << 16);
-            *(uint2*)(rowp + p0 * 2) = make_uint2(lo, hi);
-          } else {
-            uint32_t w = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 8) | (el<DT>(vst[2], e) << 16) |
-                         (el<DT>(vst[3], e) << 24);
-            *(uint32_t*)(rowp + p0) = w;
-          }
+        char* rowp = vt + (vc + e) * C::VPITCH;
+        if constexpr (DT == kBF16) {
+          const uint32_t lo = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 16);
+          const uint32_t hi = el<DT>(vst[2], e) | (el<DT>(vst[3], e) << 16);
+          *(uint2*)(rowp + vpos * 2) = make_uint2(lo, hi);
+        } else if constexpr (DT == kE4M3) {
+          *(uint32_t*)(rowp + vpos) = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 8) |
+                                      (el<DT>(vst[2], e) << 16) | (el<DT>(vst[3], e) << 24);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) *(uint32_t*)(rowp + vt_pos<KPL>(4 * vq + i) * 4) = el<DT>(vst[i], e);
@@ -358,86 +356,88 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
-
-    // ---- mainloop
+    // ---- mainloop: loads for step n+1 are in flight while step n computes
     int cur = next_step(it0);
     int buf = 0;
+    int cur_tile = 0;
     if (cur < it1) {
-      load_step(cur);
+      cur_tile = cur < T ? tile_of(cur) : 0;
+      load_step(cur, cur_tile);
       store_step(0);
     }
     __syncthreads();
-    int cur_tile = (cur < it1 && cur < T) ? prev_tile : -1;
-    if constexpr (DENSE) cur_tile = (cur < it1 && cur < T) ? T - 1 - cur : -1;
     while (cur < it1) {
       const int nxt = next_step(cur + 1);
-      if (nxt < it1) load_step(nxt);
-      int nxt_tile = (nxt < it1 && nxt < T) ? (DENSE ? T - 1 - nxt : prev_tile) : -1;
-
+      int nxt_tile = 0;
+      if (nxt < it1) {
+        nxt_tile = nxt < T ? tile_of(nxt) : 0;
+        load_step(nxt, nxt_tile);
+      }
       const char* ks = smem + buf * C::STAGE;
       const char* vt = ks + C::KBYTES;
+
       f32x16 sacc[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         sacc[jt] = f32x16{};
-        const char* arow = ks + (jt * 32 + col) * C::KPITCH + half * KPL * C::EB;
+        const char* arow = ks + (jt * 32 + col) * C::KPITCH + half * KPL * EB;
 #pragma unroll
-        for (int m = 0; m < C::NM0; ++m) {
-          Op a = lds_op<DT>(arow + m * 2 * KPL * C::EB);
-          sacc[jt] = mma<DT>(a, qf[m], sacc[jt]);
-        }
+        for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(lds_op<DT>(arow + m * 2 * KPL * EB), qf[m], sacc[jt]);
       }
-      // scale, mask, row max
-      float mloc = -INFINITY;
+      // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
+      float shift = 0.f;  // log2 units
       if (cur < T) {
         const int kbase = cur_tile * kTile;
-        const bool need_mask = kbase + kTile - 1 > t.t0;
+        if (kbase + kTile - 1 > t.t0) {  // the tile reaches past some row's position
+          const int lim = pos - kbase - 4 * half;  // key j visible iff j <= pos - kbase
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sacc[jt][r] = -INFINITY;
+        }
+      } else {
+        // blocks 64 ch + j: corrected iff J < beta and not selected; the mean stands
+        // for |B_J| = 128 keys, + ln 128 = + 7 in log2 units
+        shift = 7.f;
+        const int j0 = (cur - T) * kChunk;
+        const uint32_t w0 = selbits[j0 >> 5], w1 = selbits[(j0 >> 5) + 1];
+        const int nv = t.beta - j0;  // blocks j < nv are fully visible
+        const uint64_t okm = ~((uint64_t)w0 | ((uint64_t)w1 << 32)) &
+                             (nv >= 64 ? ~0ull : ((1ull << max(nv, 0)) - 1ull));
+        const uint64_t mine = okm >> (4 * half);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = jt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            float x = sacc[jt][r] * sl;
-            if (need_mask && kbase + j > pos) x = -INFINITY;
-            sacc[jt][r] = x;
-            mloc = fmaxf(mloc, x);
-          }
-      } else {
-        const int j0 = (cur - T) * kChunk;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const int Jb = j0 + jt * 32 + 4 * half;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int J = Jb + 8 * (r >> 2) + (r & 3);
-            const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
-            // one mean stands for |B_J| = 128 tokens: + ln 128 = + 7 in log2 units
-            float x = ok ? sacc[jt][r] * sl + 7.f : -INFINITY;
-            sacc[jt][r] = x;
-            mloc = fmaxf(mloc, x);
-          }
-        }
+          for (int r = 0; r < 16; ++r)
+            if (!((mine >> (32 * jt + 8 * (r >> 2) + (r & 3))) & 1ull)) sacc[jt][r] = -INFINITY;
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m_i, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float resc = __builtin_amdgcn_exp2f(m_i - m_use);
-      m_i = m_new;
-      float psum = 0.f;
-      constexpr float kOff = DT == kE4M3 ? 8.f : 0.f;  // P scaled onto [0, 256] for e4m3
+      float mraw = -INFINITY;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(sacc[jt][r] - m_use + kOff);
-          sacc[jt][r] = p;
-        }
+        for (int r = 0; r < 16; r += 2) mraw = fmaxf(mraw, fmaxf(sacc[jt][r], sacc[jt][r + 1]));
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+      const float m_step = mraw * sl + shift;
+      const float m_new = fmaxf(m_i, m_step);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      if (__any(m_new > m_i)) {
+        const float resc = __builtin_amdgcn_exp2f(m_i - m_use);
+        l_i *= resc;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+      }
+      m_i = m_new;
+      const float bias = shift - m_use + kOff;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], sl, bias));
 
-      // P^T as B operands of O^T += V^T P^T
+      // P^T as the B operands of O^T += V^T P^T
+      float psum = 0.f;
       Op pf[C::NM1];
       if constexpr (DT == kBF16) {
 #pragma unroll
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           bf16x8 b;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float pv = sacc[m1 >> 1][8 * (m1 & 1) + e];
+            const float pv = sacc[m1 >> 1][8 * (m1 & 1) + e];
             psum += pv;
             b[e] = static_cast<__bf16>(pv);
           }
@@ -456,10 +456,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const int jt = w >> 2, r = (w & 3) * 4;
-          uint32_t lo = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]);
-          uint32_t hi = f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]);
-          uint32_t word = lo | (hi << 16);
-          f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P ([V2] Eq. 15)
+          const uint32_t word = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]) |
+                                (f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]) << 16);
+          const f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P (Eq. 15)
           psum += (back[0] + back[1]) + (back[2] + back[3]);
           b[w] = (int)word;
         }
@@ -467,20 +466,18 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       } else {
 #pragma unroll
         for (int m1 = 0; m1 < 32; ++m1) {
-          float pv = sacc[m1 >> 4][m1 & 15];
+          const float pv = sacc[m1 >> 4][m1 & 15];
           psum += pv;
           pf[m1] = pv;
         }
       }
-      l_i = l_i * resc + psum;
+      l_i += psum;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const char* arow = vt + (nt * 32 + col) * C::VPITCH + half * KPL * C::EB;
+        const char* arow = vt + (nt * 32 + col) * C::VPITCH + half * KPL * EB;
 #pragma unroll
-        for (int m1 = 0; m1 < C::NM1; ++m1) {
-          Op a = lds_op<DT>(arow + m1 * 2 * KPL * C::EB);
-          oacc[nt] = mma<DT>(a, pf[m1], oacc[nt]);
-        }
+        for (int m1 = 0; m1 < C::NM1; ++m1)
+          oacc[nt] = mma<DT>(lds_op<DT>(arow + m1 * 2 * KPL * EB), pf[m1], oacc[nt]);
       }
       if (nxt < it1) store_step(buf ^ 1);
       __syncthreads();
@@ -490,8 +487,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     }
 
     // ---- epilogue
+    if (err) atomicOr(&g.hdr->err, (int)err);
+    const bool bad = __syncthreads_or(err != 0) != 0;
     const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
-    const bool bad = sh_bad != 0;
     if (un.nsplit == 1) {
       if (row_ok) {
         const float inv = (bad || !(l_tot > 0.f)) ? NAN : cvs / l_tot;
@@ -500,21 +498,19 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
           for (int b4 = 0; b4 < 4; ++b4) {
             const int n0 = nt * 32 + 8 * b4 + 4 * half;
-            float o0 = oacc[nt][4 * b4] * inv, o1 = oacc[nt][4 * b4 + 1] * inv;
-            float o2 = oacc[nt][4 * b4 + 2] * inv, o3 = oacc[nt][4 * b4 + 3] * inv;
+            const float o0 = oacc[nt][4 * b4] * inv, o1 = oacc[nt][4 * b4 + 1] * inv;
+            const float o2 = oacc[nt][4 * b4 + 2] * inv, o3 = oacc[nt][4 * b4 + 3] * inv;
             if constexpr (DT == kF32) {
               *(float4*)((float*)out + qrow * kD + n0) = make_float4(o0, o1, o2, o3);
             } else {
-              uint32_t w0 = f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
-              uint32_t w1 = f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
+              const uint32_t w0 = f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
+              const uint32_t w1 = f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
               *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(w0, w1);
             }
           }
-        if (lse && half == 0) {
-          constexpr float kOffL = DT == kE4M3 ? 8.f : 0.f;
+        if (lse && half == 0)
           lse[(c.row0 + pos) * g.hq + head] =
-              bad ? NAN : (m_i + __builtin_amdgcn_logf(l_tot) - kOffL) * 0.6931471805599453f;
-        }
+              bad ? NAN : (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
       }
     } else {
       // partial result of one split: O (unnormalised), m (log2), l
@@ -536,7 +532,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         pml[kRows + row_in_tile] = bad ? NAN : l_tot;
       }
     }
-    __syncthreads();
   }
 }
 
@@ -595,37 +590,50 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
 
 int attn_wgs_per_cu(int dtype) { return dtype == kF32 ? Cfg<kF32>::WGS : Cfg<kBF16>::WGS; }
 
-template <int DT, bool DENSE>
+template <int DT, bool DENSE, bool PAGED>
 static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
                                 const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* idx, const char* means, int correction, void* out,
                                 float* lse, int grid, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, PAGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<DT>::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_kernel<DT, DENSE><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
-                                                           correction, out, lse);
+  attn_kernel<DT, DENSE, PAGED><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
+                                                                  correction, out, lse);
   return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_attn_dt(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
+                                 const void* q, const void* k, const void* v, const int32_t* cu,
+                                 const int32_t* idx, const char* means, int dense, int correction,
+                                 void* out, float* lse, int grid, hipStream_t st) {
+  const bool paged = g.page_table != nullptr;
+  if (dense)
+    return paged ? launch_attn_t<DT, true, true>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st)
+                 : launch_attn_t<DT, true, false>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st);
+  return paged ? launch_attn_t<DT, false, true>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse,
+                                                grid, st)
+               : launch_attn_t<DT, false, false>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse,
+                                                 grid, st);
 }
 
 hipError_t launch_attn(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml, const void* q,
                        const void* k, const void* v, const int32_t* cu, const int32_t* idx,
                        const char* means, int dense, int correction, void* out, float* lse, int grid,
                        hipStream_t st) {
-#define FP_ATTN(DT)                                                                                   \
-  return dense ? launch_attn_t<DT, true>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st) \
-               : launch_attn_t<DT, false>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse, \
-                                          grid, st)
   switch (g.dtype) {
-    case kBF16: FP_ATTN(kBF16);
-    case kF32: FP_ATTN(kF32);
-    default: FP_ATTN(kE4M3);
+    case kBF16:
+      return launch_attn_dt<kBF16>(g, wl, ws, ml, q, k, v, cu, idx, means, dense, correction, out, lse, grid, st);
+    case kF32:
+      return launch_attn_dt<kF32>(g, wl, ws, ml, q, k, v, cu, idx, means, dense, correction, out, lse, grid, st);
+    default:
+      return launch_attn_dt<kE4M3>(g, wl, ws, ml, q, k, v, cu, idx, means, dense, correction, out, lse, grid, st);
   }
-#undef FP_ATTN
 }
 
 hipError_t launch_combine(const Geo& g, const WsLayout& wl, char* ws, void* out, float* lse, hipStream_t st) {

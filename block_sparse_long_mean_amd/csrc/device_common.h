@@ -56,6 +56,17 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
 // Segment s -> (request b, kv head h, tile I) through the per-request segment
 // offsets (binary search; segments are ordered request, kv head, tile).
 struct SegCoord {

@@ -64,7 +64,7 @@ struct MeansLayout {
 
 // Layout of the workspace (byte offsets).
 struct WsLayout {
-  size_t hdr, seg_off, blk_base, counts, bits, hist, cursor, units, part_o, part_ml, total;
+  size_t hdr, seg_off, blk_base, counts, scan_part, bits, hist, cursor, units, part_o, part_ml, total;
   int32_t umax;           // largest split count of one segment
 };
 
@@ -80,7 +80,7 @@ hipError_t launch_pool(const Geo& g, const MeansLayout& ml, const void* k, const
 hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* q,
                                const char* means, float alpha, int sink, int win,
                                int32_t* counts, uint32_t* bits, float* energies, hipStream_t st);
-hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, hipStream_t st);
+hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, int32_t* part, hipStream_t st);
 hipError_t launch_expand(const Geo& g, const int32_t* cu, const uint32_t* bits, int32_t* idx,
                          int64_t cap, hipStream_t st);
 hipError_t launch_sched(const Geo& g, const WsLayout& wl, char* ws, const int32_t* cu,

@@ -36,15 +36,40 @@ __global__ __launch_bounds__(256) void sched_zero_kernel(int32_t* hist) {
   for (int i = threadIdx.x + blockIdx.x * 256; i < kBuckets; i += 256 * gridDim.x) hist[i] = 0;
 }
 
+// Lanes of a wave that share a bucket are served by one atomic: the lowest
+// such lane adds their total, and each lane gets its own offset from a
+// masked prefix sum.  Returns the lane's base (scatter) or 0 (count).
+__device__ __forceinline__ int bucket_add(int32_t* ctr, bool active, int key, int amount) {
+  int base_out = 0;
+  uint64_t pending = __ballot(active);
+  const int lane = threadIdx.x & 63;
+  while (pending) {
+    const int leader = __ffsll((long long)pending) - 1;
+    const int lkey = __shfl(key, leader, 64);
+    const bool mine = active && key == lkey && ((pending >> lane) & 1ull);
+    const int contrib = mine ? amount : 0;
+    const int incl = wave_incl_scan(contrib);
+    const int total = __shfl(incl, 63, 64);
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&ctr[lkey], total);
+    base = __shfl(base, leader, 64);
+    if (mine) base_out = base + incl - contrib;
+    pending &= ~__ballot(mine);
+  }
+  return base_out;
+}
+
 __global__ __launch_bounds__(256) void sched_count_kernel(Geo g, const int32_t* __restrict__ cu, int dense,
                                                           int correction, SplitPolicy sp, int32_t* hist,
                                                           int32_t* nsplit) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (s >= g.n_seg) return;
-  int U, key;
-  seg_work(g, cu, s, dense, correction, sp, U, key);
-  nsplit[s] = U;
-  atomicAdd(&hist[key], U);
+  const bool active = s < g.n_seg;
+  int U = 0, key = 0;
+  if (active) {
+    seg_work(g, cu, s, dense, correction, sp, U, key);
+    nsplit[s] = U;
+  }
+  bucket_add(hist, active, key, U);
 }
 
 // Descending exclusive scan of the bucket histogram (one workgroup).
@@ -80,11 +105,12 @@ __global__ __launch_bounds__(256) void sched_scatter_kernel(Geo g, const int32_t
                                                             int correction, SplitPolicy sp, int32_t* cursor,
                                                             int2* units) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (s >= g.n_seg) return;
-  int U, key;
-  seg_work(g, cu, s, dense, correction, sp, U, key);
-  const int base = atomicAdd(&cursor[key], U);
-  for (int u = 0; u < U; ++u) units[base + u] = make_int2((int)s, u | (U << 16));
+  const bool active = s < g.n_seg;
+  int U = 0, key = 0;
+  if (active) seg_work(g, cu, s, dense, correction, sp, U, key);
+  const int base = bucket_add(cursor, active, key, U);
+  if (active)
+    for (int u = 0; u < U; ++u) units[base + u] = make_int2((int)s, u | (U << 16));
 }
 
 hipError_t launch_sched(const Geo& g, const WsLayout& wl, char* ws, const int32_t* cu, int dense,

@@ -212,29 +212,54 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   }
 }
 
-// Exclusive prefix sum of the per-segment counts into cu[n+1] (one workgroup).
-__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ counts, int64_t n,
-                                                   int32_t* __restrict__ cu) {
-  __shared__ int64_t part[1024];
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = tid * per, hi = min(lo + per, n);
-  int64_t loc = 0;
-  for (int64_t i = lo; i < hi; ++i) loc += counts[i];
-  part[tid] = loc;
+// Exclusive prefix sum of the per-segment counts into cu[n+1], in two
+// passes: 1024-entry blocks reduce to partial sums (scan_part_kernel), then
+// every block rescans its entries on top of the sum of the partials before it.
+__device__ __forceinline__ int block_excl_scan_1024(int x, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) sh[w] = incl;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int64_t a = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += a;
-    __syncthreads();
+  if (w == 0) {
+    int v = lane < 16 ? sh[lane] : 0;
+    int vi = wave_incl_scan(v);
+    if (lane < 16) sh[16 + lane] = vi - v;
+    if (lane == 15) sh[32] = vi;
   }
-  int64_t run = part[tid] - loc;
-  for (int64_t i = lo; i < hi; ++i) {
-    cu[i] = (int32_t)run;
-    run += counts[i];
+  __syncthreads();
+  total = sh[32];
+  const int r = sh[16 + w] + incl - x;
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void scan_part_kernel(const int32_t* __restrict__ counts, int64_t n,
+                                                         int32_t* __restrict__ part) {
+  __shared__ int sh[40];
+  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  int total;
+  block_excl_scan_1024(i < n ? counts[i] : 0, sh, total);
+  if (threadIdx.x == 0) part[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restrict__ counts, int64_t n,
+                                                          const int32_t* __restrict__ part, int32_t* __restrict__ cu) {
+  __shared__ int sh[40];
+  __shared__ int base_sh;
+  // offset of this block: sum of the partials before it (one wave)
+  if (threadIdx.x < 64) {
+    int acc = 0;
+    for (int b = threadIdx.x; b < (int)blockIdx.x; b += 64) acc += part[b];
+    acc = wave_sum_i(acc);
+    if (threadIdx.x == 0) base_sh = acc;
   }
-  if (tid == 1023) cu[n] = (int32_t)part[1023];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const int x = i < n ? counts[i] : 0;
+  int total;
+  const int ex = block_excl_scan_1024(x, sh, total);
+  if (i < n) cu[i] = base_sh + ex;
+  if (i == n - 1) cu[n] = base_sh + ex + x;
 }
 
 // One wave per segment: ballot + prefix count turn the selection bits into the
@@ -298,8 +323,10 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, hipStream_t st) {
-  scan_kernel<<<1, 1024, 0, st>>>(counts, n, cu);
+hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, int32_t* part, hipStream_t st) {
+  const unsigned nb = (unsigned)((n + 1023) / 1024);
+  scan_part_kernel<<<nb, 1024, 0, st>>>(counts, n, part);
+  scan_final_kernel<<<nb, 1024, 0, st>>>(counts, n, part, cu);
   return hipGetLastError();
 }
 
