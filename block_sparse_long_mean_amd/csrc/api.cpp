@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -146,6 +147,11 @@ SplitPolicy split_policy(const fp_problem* p, const HostGeo& hg) {
   int64_t u = hg.n_seg > 0 ? (4 * slots + hg.n_seg - 1) / hg.n_seg : 1;
   sp.umax = (int32_t)std::max<int64_t>(1, std::min<int64_t>(16, u));
   sp.min_split = 4;
+  // FP_MAX_SPLITS caps the split count of a segment (1 disables KV splitting)
+  if (const char* e = std::getenv("FP_MAX_SPLITS")) {
+    const int cap = std::atoi(e);
+    if (cap >= 1) sp.umax = std::min<int32_t>(sp.umax, std::min(cap, 16));
+  }
   return sp;
 }
 

@@ -84,7 +84,8 @@ struct Cfg {
   static constexpr int VPITCH = kTile * EB + 16; // bytes per staged V^T row
   static constexpr int KBYTES = kTile * KPITCH;
   static constexpr int VBYTES = kD * VPITCH;
-  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int PENBYTES = 2 * 32 * 4;    // correction-step logit offsets, per lane half
+  static constexpr int STAGE = KBYTES + VBYTES + PENBYTES;
   static constexpr int LDS = 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
   static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
   static constexpr int NM1 = kTile / (2 * KPL);  // MFMAs per 32-column output tile
@@ -147,24 +148,56 @@ struct Unit {
   int split, nsplit;
 };
 
-// Offset (in head vectors, i.e. row * hkv + h) of token j of the segment's
-// request.  PAGED: through the page table ([V2] Eq. 22); an entry outside
-// the pool sets kErrPage in err and reads row 0 instead.
-template <bool PAGED>
-__device__ __forceinline__ int64_t tok_vec(const Geo& g, const SegCoord& c, int j, uint32_t& err) {
-  if constexpr (!PAGED) {
-    return (c.row0 + j) * g.hkv + c.h;
+// K/V addressing modes of the attention kernel.
+enum AddrMode : int {
+  kContig = 0,    // K/V rows follow Q rows; one buffer resource per (request, kv head)
+  kPagedTile = 1, // page size a multiple of 64: a 64-key tile lies inside one page
+  kPagedAny = 2,  // any page size: one page-table lookup per key row ([V2] Eq. 22)
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufFlags = 0x00020000;  // raw dword buffer, range-checked
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const int n = bytes >= 0xffffffffull ? (int)0xffffffffu : (int)(uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufFlags);
+}
+
+// 8 consecutive elements of one K/V/mean row through a buffer resource
+// (out-of-range offsets read as zero).
+template <int DT>
+__device__ __forceinline__ void bld8(Vec8<DT>& o, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (DT == kBF16) {
+    u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    o.w[0] = a[0]; o.w[1] = a[1]; o.w[2] = a[2]; o.w[3] = a[3];
+  } else if constexpr (DT == kE4M3) {
+    u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    o.w[0] = a[0]; o.w[1] = a[1];
   } else {
-    const int pg = j / g.page_size;
-    const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
-    const int64_t slot = page * g.page_size + (j - pg * g.page_size);
-    const bool ok = page >= 0 && slot < g.num_slots;
-    err |= ok ? 0u : (uint32_t)kErrPage;
-    return (ok ? slot : 0) * g.hkv + c.h;
+    u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff + 16, (int)soff, 0);
+    o.w[0] = a[0]; o.w[1] = a[1]; o.w[2] = a[2]; o.w[3] = a[3];
+    o.w[4] = b[0]; o.w[5] = b[1]; o.w[6] = b[2]; o.w[7] = b[3];
   }
 }
 
-template <int DT, bool DENSE, bool PAGED>
+// Byte offset of token j's vector in the paged pool (one lookup, [V2] Eq. 22);
+// an entry outside the pool sets kErrPage and reads slot 0.
+__device__ __forceinline__ uint32_t paged_off(const Geo& g, const SegCoord& c, int j, uint32_t rowstride,
+                                              uint32_t& err) {
+  const int pg = j / g.page_size;
+  const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+  const int64_t slot = page * g.page_size + (j - pg * g.page_size);
+  const bool ok = page >= 0 && slot < g.num_slots;
+  err |= ok ? 0u : (uint32_t)kErrPage;
+  return (uint32_t)(ok ? slot : 0) * rowstride;
+}
+
+constexpr uint32_t kNaN32 = 0x7fc00000u;
+constexpr uint32_t kNaNbf16x2 = 0x7fc07fc0u;
+
+template <int DT, bool DENSE, int AM>
 __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     Geo g, WsLayout wl, char* __restrict__ ws, MeansLayout ml, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ cu,
@@ -186,12 +219,19 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
                    (DT == kE4M3 ? g.descale[0] * g.descale[1] : 1.f);
   const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
   constexpr float kOff = DT == kE4M3 ? 8.f : 0.f;  // e4m3: P scaled onto [0, 256] (Eq. 15)
+  const uint32_t rowstride = (uint32_t)g.hkv * kD * EB;  // bytes from one token to the next
 
   // staging assignment: K rows kr + 16 i, columns kc..kc+7 (16 lanes per row);
   // V key quad vq (keys 4vq..4vq+3), columns vc..vc+7 (16 lanes per V^T row)
   const int kr = tid >> 4, kc = (tid & 15) * 8;
   const int vq = tid & 15, vc = (tid >> 4) * 8;
   const int vpos = vt_pos<KPL>(4 * vq);
+  uint32_t voff_k[4], voff_v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    voff_k[i] = (uint32_t)(kr + 16 * i) * rowstride + kc * EB;
+    voff_v[i] = (uint32_t)(4 * vq + i) * rowstride + vc * EB;
+  }
 
   for (;;) {
     if (tid == 0) sh_unit = atomicAdd(&g.hdr->work_counter, 1);
@@ -219,8 +259,31 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const int per = (W + un.nsplit - 1) / un.nsplit;
     const int it0 = min(W, un.split * per), it1 = min(W, it0 + per);
 
+    // K/V and pooled-means base addresses of this unit.  Each step builds its
+    // buffer resources from base + step offset with the remaining bytes as the
+    // range (the range check covers the per-lane offset only), so keys past the
+    // end of the request read as zero in the contiguous layout.
+    const char* kbase;
+    const char* vbase;
+    uint64_t kvbytes;
+    if constexpr (AM == kContig) {
+      const uint64_t base = ((uint64_t)c.row0 * g.hkv + c.h) * kD * EB;
+      kbase = (const char*)k + base;
+      vbase = (const char*)v + base;
+      kvbytes = c.L > 0 ? (uint64_t)(c.L - 1) * rowstride + kD * EB : 0;
+    } else {
+      const uint64_t base = (uint64_t)c.h * kD * EB;
+      kbase = (const char*)k + base;
+      vbase = (const char*)v + base;
+      kvbytes = (uint64_t)(g.num_slots - 1) * rowstride + kD * EB;
+    }
+    const uint64_t mbase = ((uint64_t)g.blk_base[c.b] * g.hkv + c.h) * kD * EB;
+    const char* kmbase = means + ml.kop + mbase;
+    const char* vmbase = means + ml.vop + mbase;
+    const uint64_t mbytes = (uint64_t)(((t.beta + kChunk - 1) / kChunk) * kChunk) * rowstride;
+
     if (NC > 0) {
-      for (int w = tid; w <= (t.beta >> 5); w += 256) selbits[w] = 0;
+      for (int w = tid; w <= (t.beta >> 5) + 2; w += 256) selbits[w] = 0;
       __syncthreads();
       for (int e = tid; e < T; e += 256) {
         const int J = idx[seg0 + e] >> 1;
@@ -298,32 +361,61 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     Vec8<DT> kst[4], vst[4];
     auto load_step = [&](int it, int p) {
       if (it < T) {
-        const char* kb = (const char*)k + (int64_t)kc * EB;
-        const char* vb = (const char*)v + (int64_t)vc * EB;
+        const int j0 = p * kTile;
+        if constexpr (AM == kContig) {
+          const uint64_t o = (uint64_t)j0 * rowstride;
+          const uint64_t left = kvbytes > o ? kvbytes - o : 0;
+          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // tokens past the end of the request are causally masked for every
-          // row; reading the last token keeps V finite
-          const int jk = min(p * kTile + kr + 16 * i, c.L - 1);
-          const int jv = min(p * kTile + 4 * vq + i, c.L - 1);
-          ld8<DT>(kst[i], kb + tok_vec<PAGED>(g, c, jk, err) * (kD * EB));
-          ld8<DT>(vst[i], vb + tok_vec<PAGED>(g, c, jv, err) * (kD * EB));
+          for (int i = 0; i < 4; ++i) {
+            bld8<DT>(kst[i], rk, voff_k[i], 0);
+            bld8<DT>(vst[i], rv, voff_v[i], 0);
+          }
+        } else if constexpr (AM == kPagedTile) {
+          const int pg = j0 / g.page_size;
+          const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+          int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
+          if (page < 0 || slot0 + kTile > g.num_slots) {
+            err |= kErrPage;
+            slot0 = 0;
+          }
+          const uint64_t o = (uint64_t)slot0 * rowstride;
+          const uint64_t left = kvbytes > o ? kvbytes - o : 0;
+          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bld8<DT>(kst[i], rk, voff_k[i], 0);
+            bld8<DT>(vst[i], rv, voff_v[i], 0);
+          }
+          if (j0 + kTile > c.L) {  // the request's last tile: slots past its end may hold anything
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (j0 + 4 * vq + i >= c.L) zero8<DT>(vst[i]);
+          }
+        } else {
+          const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, kvbytes), rv = make_rsrc(vbase, kvbytes);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int jk = min(j0 + kr + 16 * i, c.L - 1);
+            const int jv = min(j0 + 4 * vq + i, c.L - 1);
+            bld8<DT>(kst[i], rk, paged_off(g, c, jk, rowstride, err) + kc * EB, 0);
+            bld8<DT>(vst[i], rv, paged_off(g, c, jv, rowstride, err) + vc * EB, 0);
+          }
         }
       } else {
-        // pooled means of blocks 64 ch .. 64 ch + 63 (the padded arrays hold
-        // zeros past the request's last block)
-        const int64_t mb = ((int64_t)g.blk_base[c.b] + (it - T) * kChunk) * g.hkv + c.h;
-        const char* kb = means + ml.kop + (int64_t)kc * EB;
-        const char* vb = means + ml.vop + (int64_t)vc * EB;
+        // pooled means of blocks 64 ch .. 64 ch + 63 (past beta they are masked)
+        const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
+        const uint64_t left = mbytes > o ? mbytes - o : 0;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kmbase + o, left), rv = make_rsrc(vmbase + o, left);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          ld8<DT>(kst[i], kb + (mb + (int64_t)(kr + 16 * i) * g.hkv) * (kD * EB));
-          ld8<DT>(vst[i], vb + (mb + (int64_t)(4 * vq + i) * g.hkv) * (kD * EB));
+          bld8<DT>(kst[i], rk, voff_k[i], 0);
+          bld8<DT>(vst[i], rv, voff_v[i], 0);
         }
       }
     };
 
-    auto store_step = [&](int buf) {
+    auto store_step = [&](int buf, int it) {
       char* ks = smem + buf * C::STAGE;
       char* vt = ks + C::KBYTES;
 #pragma unroll
@@ -343,16 +435,31 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       for (int e = 0; e < 8; ++e) {
         char* rowp = vt + (vc + e) * C::VPITCH;
         if constexpr (DT == kBF16) {
-          const uint32_t lo = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 16);
-          const uint32_t hi = el<DT>(vst[2], e) | (el<DT>(vst[3], e) << 16);
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo = __builtin_amdgcn_perm(vst[1].w[e >> 1], vst[0].w[e >> 1], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vst[3].w[e >> 1], vst[2].w[e >> 1], sel);
           *(uint2*)(rowp + vpos * 2) = make_uint2(lo, hi);
         } else if constexpr (DT == kE4M3) {
-          *(uint32_t*)(rowp + vpos) = el<DT>(vst[0], e) | (el<DT>(vst[1], e) << 8) |
-                                      (el<DT>(vst[2], e) << 16) | (el<DT>(vst[3], e) << 24);
+          const int b = e & 3;
+          const uint32_t sel = 0x0c0c0400u | (uint32_t)b | ((uint32_t)b << 8);
+          const uint32_t lo = __builtin_amdgcn_perm(vst[1].w[e >> 2], vst[0].w[e >> 2], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(vst[3].w[e >> 2], vst[2].w[e >> 2], sel);
+          *(uint32_t*)(rowp + vpos) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) *(uint32_t*)(rowp + vt_pos<KPL>(4 * vq + i) * 4) = el<DT>(vst[i], e);
         }
+      }
+      if (it >= T && tid < 64) {
+        // logit offset of each register of a correction step, per lane half:
+        // + 7 (ln 128 in log2 units) where the block is corrected, -inf where it is
+        // selected or not fully visible to the tile
+        float* pen = (float*)(vt + C::VBYTES);
+        const int h = tid >> 5, k = tid & 31;
+        const int rho = 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * h + (k & 3);
+        const int J = (it - T) * kChunk + rho;
+        const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
+        pen[tid] = ok ? 7.f : -INFINITY;
       }
     };
 
@@ -363,7 +470,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if (cur < it1) {
       cur_tile = cur < T ? tile_of(cur) : 0;
       load_step(cur, cur_tile);
-      store_step(0);
+      store_step(0, cur);
     }
     __syncthreads();
     while (cur < it1) {
@@ -385,8 +492,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(lds_op<DT>(arow + m * 2 * KPL * EB), qf[m], sacc[jt]);
       }
       // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
-      float shift = 0.f;  // log2 units
-      if (cur < T) {
+      float m_step;
+      const bool chunk = cur >= T;
+      if (!chunk) {
         const int kbase = cur_tile * kTile;
         if (kbase + kTile - 1 > t.t0) {  // the tile reaches past some row's position
           const int lim = pos - kbase - 4 * half;  // key j visible iff j <= pos - kbase
@@ -396,29 +504,30 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             for (int r = 0; r < 16; ++r)
               if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sacc[jt][r] = -INFINITY;
         }
-      } else {
-        // blocks 64 ch + j: corrected iff J < beta and not selected; the mean stands
-        // for |B_J| = 128 keys, + ln 128 = + 7 in log2 units
-        shift = 7.f;
-        const int j0 = (cur - T) * kChunk;
-        const uint32_t w0 = selbits[j0 >> 5], w1 = selbits[(j0 >> 5) + 1];
-        const int nv = t.beta - j0;  // blocks j < nv are fully visible
-        const uint64_t okm = ~((uint64_t)w0 | ((uint64_t)w1 << 32)) &
-                             (nv >= 64 ? ~0ull : ((1ull << max(nv, 0)) - 1ull));
-        const uint64_t mine = okm >> (4 * half);
+        float mraw = -INFINITY;
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (!((mine >> (32 * jt + 8 * (r >> 2) + (r & 3))) & 1ull)) sacc[jt][r] = -INFINITY;
+          for (int r = 0; r < 16; r += 2) mraw = fmaxf(mraw, fmaxf(sacc[jt][r], sacc[jt][r + 1]));
+        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+        m_step = mraw * sl;
+      } else {
+        const f32x4* pen = (const f32x4*)(vt + C::VBYTES) + half * 8;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 pv = pen[jt * 4 + r4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = fmaf(sacc[jt][4 * r4 + e], sl, pv[e]);
+              sacc[jt][4 * r4 + e] = x;
+              mx = fmaxf(mx, x);
+            }
+          }
+        m_step = fmaxf(mx, __shfl_xor(mx, 32, 64));
       }
-      float mraw = -INFINITY;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mraw = fmaxf(mraw, fmaxf(sacc[jt][r], sacc[jt][r + 1]));
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
-      const float m_step = mraw * sl + shift;
       const float m_new = fmaxf(m_i, m_step);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       if (__any(m_new > m_i)) {
@@ -430,11 +539,17 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
       }
       m_i = m_new;
-      const float bias = shift - m_use + kOff;
+      if (!chunk) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], sl, bias));
+          for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], sl, kOff - m_use));
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(sacc[jt][r] + (kOff - m_use));
+      }
 
       // P^T as the B operands of O^T += V^T P^T
       float psum = 0.f;
@@ -479,57 +594,83 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         for (int m1 = 0; m1 < C::NM1; ++m1)
           oacc[nt] = mma<DT>(lds_op<DT>(arow + m1 * 2 * KPL * EB), pf[m1], oacc[nt]);
       }
-      if (nxt < it1) store_step(buf ^ 1);
+      if (nxt < it1) store_step(buf ^ 1, nxt);
       __syncthreads();
       buf ^= 1;
       cur = nxt;
       cur_tile = nxt_tile;
     }
 
-    // ---- epilogue
+    // ---- epilogue: results as floats; a unit that saw malformed input stores
+    // NaN bit patterns instead (a separate branch, so no float select is involved)
     if (err) atomicOr(&g.hdr->err, (int)err);
     const bool bad = __syncthreads_or(err != 0) != 0;
     const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
     if (un.nsplit == 1) {
       if (row_ok) {
-        const float inv = (bad || !(l_tot > 0.f)) ? NAN : cvs / l_tot;
+        if (!bad) {
+          const float inv = cvs / l_tot;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+          for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int b4 = 0; b4 < 4; ++b4) {
-            const int n0 = nt * 32 + 8 * b4 + 4 * half;
-            const float o0 = oacc[nt][4 * b4] * inv, o1 = oacc[nt][4 * b4 + 1] * inv;
-            const float o2 = oacc[nt][4 * b4 + 2] * inv, o3 = oacc[nt][4 * b4 + 3] * inv;
-            if constexpr (DT == kF32) {
-              *(float4*)((float*)out + qrow * kD + n0) = make_float4(o0, o1, o2, o3);
-            } else {
-              const uint32_t w0 = f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
-              const uint32_t w1 = f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
-              *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(w0, w1);
+            for (int b4 = 0; b4 < 4; ++b4) {
+              const int n0 = nt * 32 + 8 * b4 + 4 * half;
+              const float o0 = oacc[nt][4 * b4] * inv, o1 = oacc[nt][4 * b4 + 1] * inv;
+              const float o2 = oacc[nt][4 * b4 + 2] * inv, o3 = oacc[nt][4 * b4 + 3] * inv;
+              if constexpr (DT == kF32) {
+                *(float4*)((float*)out + qrow * kD + n0) = make_float4(o0, o1, o2, o3);
+              } else {
+                const uint32_t w0 = f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
+                const uint32_t w1 = f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
+                *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(w0, w1);
+              }
             }
-          }
-        if (lse && half == 0)
-          lse[(c.row0 + pos) * g.hq + head] =
-              bad ? NAN : (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
+          if (lse && half == 0)
+            lse[(c.row0 + pos) * g.hq + head] =
+                (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) {
+              const int n0 = nt * 32 + 8 * b4 + 4 * half;
+              if constexpr (DT == kF32)
+                *(uint4*)((float*)out + qrow * kD + n0) = make_uint4(kNaN32, kNaN32, kNaN32, kNaN32);
+              else
+                *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(kNaNbf16x2, kNaNbf16x2);
+            }
+          if (lse && half == 0) ((uint32_t*)lse)[(c.row0 + pos) * g.hq + head] = kNaN32;
+        }
       }
     } else {
       // partial result of one split: O (unnormalised), m (log2), l
       const int64_t slot = un.s * wl.umax + un.split;
       float* po = (float*)(ws + wl.part_o) + slot * kRows * kD;
       float* pml = (float*)(ws + wl.part_ml) + slot * 2 * kRows;
+      if (!bad) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-          const int n0 = nt * 32 + 8 * b4 + 4 * half;
-          float4 val = make_float4(oacc[nt][4 * b4], oacc[nt][4 * b4 + 1], oacc[nt][4 * b4 + 2],
-                                   oacc[nt][4 * b4 + 3]);
-          if (bad) val = make_float4(NAN, NAN, NAN, NAN);
-          *(float4*)(po + row_in_tile * kD + n0) = val;
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int n0 = nt * 32 + 8 * b4 + 4 * half;
+            *(float4*)(po + row_in_tile * kD + n0) =
+                make_float4(oacc[nt][4 * b4], oacc[nt][4 * b4 + 1], oacc[nt][4 * b4 + 2], oacc[nt][4 * b4 + 3]);
+          }
+        if (half == 0) {
+          pml[row_in_tile] = m_i;
+          pml[kRows + row_in_tile] = l_tot;
         }
-      if (half == 0) {
-        pml[row_in_tile] = m_i;
-        pml[kRows + row_in_tile] = bad ? NAN : l_tot;
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4)
+            *(uint4*)(po + row_in_tile * kD + nt * 32 + 8 * b4 + 4 * half) =
+                make_uint4(kNaN32, kNaN32, kNaN32, kNaN32);
+        if (half == 0) {
+          pml[row_in_tile] = m_i;
+          ((uint32_t*)pml)[kRows + row_in_tile] = kNaN32;
+        }
       }
     }
   }
@@ -590,19 +731,19 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
 
 int attn_wgs_per_cu(int dtype) { return dtype == kF32 ? Cfg<kF32>::WGS : Cfg<kBF16>::WGS; }
 
-template <int DT, bool DENSE, bool PAGED>
+template <int DT, bool DENSE, int AM>
 static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
                                 const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* idx, const char* means, int correction, void* out,
                                 float* lse, int grid, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, PAGED>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, AM>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<DT>::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_kernel<DT, DENSE, PAGED><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
+  attn_kernel<DT, DENSE, AM><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
                                                                   correction, out, lse);
   return hipGetLastError();
 }
@@ -612,14 +753,12 @@ static hipError_t launch_attn_dt(const Geo& g, const WsLayout& wl, char* ws, con
                                  const void* q, const void* k, const void* v, const int32_t* cu,
                                  const int32_t* idx, const char* means, int dense, int correction,
                                  void* out, float* lse, int grid, hipStream_t st) {
-  const bool paged = g.page_table != nullptr;
-  if (dense)
-    return paged ? launch_attn_t<DT, true, true>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st)
-                 : launch_attn_t<DT, true, false>(g, wl, ws, ml, q, k, v, cu, idx, means, 0, out, lse, grid, st);
-  return paged ? launch_attn_t<DT, false, true>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse,
-                                                grid, st)
-               : launch_attn_t<DT, false, false>(g, wl, ws, ml, q, k, v, cu, idx, means, correction, out, lse,
-                                                 grid, st);
+  const int am = !g.page_table ? kContig : (g.page_size % kTile == 0 ? kPagedTile : kPagedAny);
+#define FP_AM(DENSE, AMV) \
+  launch_attn_t<DT, DENSE, AMV>(g, wl, ws, ml, q, k, v, cu, idx, means, DENSE ? 0 : correction, out, lse, grid, st)
+  if (dense) return am == kContig ? FP_AM(true, kContig) : am == kPagedTile ? FP_AM(true, kPagedTile) : FP_AM(true, kPagedAny);
+  return am == kContig ? FP_AM(false, kContig) : am == kPagedTile ? FP_AM(false, kPagedTile) : FP_AM(false, kPagedAny);
+#undef FP_AM
 }
 
 hipError_t launch_attn(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml, const void* q,
