@@ -80,17 +80,56 @@ template <int DT>
 struct Cfg {
   static constexpr int EB = Tr<DT>::EB;
   static constexpr int KPL = Tr<DT>::KPL;
-  static constexpr int KPITCH = kD * EB + 16;    // bytes per staged K row
-  static constexpr int VPITCH = kTile * EB + 16; // bytes per staged V^T row
+  // bf16 / e4m3: K and V rows go HBM -> LDS by DMA, unpadded with XOR-swizzled
+  // 16-byte chunks; V stays row-major and is read transposed.  fp32: rows are
+  // staged through registers, V is written transposed, rows are padded.
+  static constexpr bool DMA = DT != kF32;
+  static constexpr int ROWB = kD * EB;                         // bytes of one K/V row
+  static constexpr int KPITCH = DMA ? ROWB : ROWB + 16;        // bytes per staged K row
+  static constexpr int VPITCH = DMA ? ROWB : kTile * EB + 16;  // V row (DMA) or V^T row (fp32)
   static constexpr int KBYTES = kTile * KPITCH;
-  static constexpr int VBYTES = kD * VPITCH;
+  static constexpr int VBYTES = DMA ? kTile * VPITCH : kD * VPITCH;
   static constexpr int PENBYTES = 2 * 32 * 4;    // correction-step logit offsets, per lane half
   static constexpr int STAGE = KBYTES + VBYTES + PENBYTES;
   static constexpr int LDS = 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
   static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
   static constexpr int NM1 = kTile / (2 * KPL);  // MFMAs per 32-column output tile
   static constexpr int WGS = DT == kF32 ? 1 : 2; // workgroups per CU
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;           // rows written by one 1 KB DMA instruction
+  static constexpr int NDMA = kTile / RPI / 4;   // DMA instructions per wave per K (or V) tile
 };
+
+// XOR swizzles of the 16-byte chunks of a staged row, chosen so that the
+// MFMA operand reads hit distinct LDS banks: K rows are read 16 rows at a
+// time at one chunk; V rows are read by the transpose loads 4 (bf16) or 8
+// (e4m3) rows at a time at one or two chunks.
+template <int DT>
+__device__ __forceinline__ int swz_k(int r) {
+  return DT == kBF16 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int DT>
+__device__ __forceinline__ int swz_v(int r) {
+  return DT == kBF16 ? 4 * (r & 3) : 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// 16 bytes per lane from a buffer resource straight into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, (int)voff, 0, 0, 0);
+}
+// Transpose reads (see the operand builders below for the lane layout).
+__device__ __forceinline__ i16x4 lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+__device__ __forceinline__ i32x2 lds_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+// Wait for this wave's outstanding vector-memory loads (including LDS DMA).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Position in a staged V^T row of key j (0..63) of the tile: keys are laid
 // out in the order in which each lane half holds the probabilities of the
@@ -236,7 +275,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   for (;;) {
     if (tid == 0) sh_unit = atomicAdd(&g.hdr->work_counter, 1);
     __syncthreads();
-    const int u = sh_unit;
+    // the unit id is wave-uniform; saying so keeps every value derived from it
+    // (segment geometry, base addresses, buffer resources) in scalar registers
+    const int u = __builtin_amdgcn_readfirstlane(sh_unit);
     if (u >= g.hdr->total_units) break;
     const int2 ud = units[u];
     const Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
@@ -337,7 +378,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     };
     auto next_step = [&](int it) -> int {
       while (it < it1 && it >= T && !chunk_todo(it - T)) ++it;
-      return it;
+      return __builtin_amdgcn_readfirstlane(it);  // uniform: every lane reads the same bits
     };
     // strictly ascending list: a split also checks the entry its predecessor saw last
     int prev_tile = 1 << 30;
@@ -348,7 +389,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       if constexpr (DENSE) {
         return T - 1 - it;
       } else {
-        int p = idx[seg0 + T - 1 - it];
+        int p = __builtin_amdgcn_readfirstlane(idx[seg0 + T - 1 - it]);
         if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
           err |= kErrIdx;
           p = 0;
@@ -358,18 +399,83 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
-    Vec8<DT> kst[4], vst[4];
-    auto load_step = [&](int it, int p) {
+    // per-lane DMA offsets within a 64-row tile (bf16/e4m3): instruction q of
+    // wave w fills rows 16w + RPI q + lane / CPR, chunk lane % CPR, which holds
+    // the row's logical chunk (lane % CPR) ^ swizzle(row)
+    uint32_t dk[C::NDMA > 0 ? C::NDMA : 1], dv[C::NDMA > 0 ? C::NDMA : 1];
+    if constexpr (C::DMA) {
+#pragma unroll
+      for (int qq = 0; qq < C::NDMA; ++qq) {
+        const int r = 16 * wave + C::RPI * qq + lane / C::CPR;
+        const int cl = lane % C::CPR;
+        dk[qq] = (uint32_t)r * rowstride + (uint32_t)((cl ^ swz_k<DT>(r)) * 16);
+        dv[qq] = (uint32_t)r * rowstride + (uint32_t)((cl ^ swz_v<DT>(r)) * 16);
+      }
+    }
+    Vec8<DT> kst[C::DMA ? 1 : 4], vst[C::DMA ? 1 : 4];
+
+    // DMA of one 64-row K and V tile (rows past the range read as zero)
+    auto dma_tile = [&](int buf, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv) {
+      char* ks = smem + buf * C::STAGE;
+      char* vs = ks + C::KBYTES;
+#pragma unroll
+      for (int qq = 0; qq < C::NDMA; ++qq) {
+        const int r0 = 16 * wave + C::RPI * qq;
+        dma16(rk, ks + r0 * C::ROWB, dk[qq]);
+        dma16(rv, vs + r0 * C::ROWB, dv[qq]);
+      }
+    };
+    // paged, any page size: one page-table lookup per row; rows past the request
+    // get an offset outside the range and read as zero
+    auto dma_tile_rows = [&](int buf, int j0, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv) {
+      char* ks = smem + buf * C::STAGE;
+      char* vs = ks + C::KBYTES;
+#pragma unroll
+      for (int qq = 0; qq < C::NDMA; ++qq) {
+        const int r = 16 * wave + C::RPI * qq + lane / C::CPR;
+        const int cl = lane % C::CPR;
+        const int j = j0 + r;
+        uint32_t base = 0xfffffff0u;
+        if (j < c.L) base = paged_off(g, c, j, rowstride, err);
+        const uint32_t ok = j < c.L ? 0u : 0xfffffff0u;
+        const uint32_t ok_k = ok ? ok : base + (uint32_t)((cl ^ swz_k<DT>(r)) * 16);
+        const uint32_t ok_v = ok ? ok : base + (uint32_t)((cl ^ swz_v<DT>(r)) * 16);
+        const int r0 = 16 * wave + C::RPI * qq;
+        dma16(rk, ks + r0 * C::ROWB, ok_k);
+        dma16(rv, vs + r0 * C::ROWB, ok_v);
+      }
+    };
+
+    auto write_pen = [&](int buf, int it) {
+      if (it >= T && tid < 64) {
+        // logit offset of each register of a correction step, per lane half:
+        // + 7 (ln 128 in log2 units) where the block is corrected, -inf where it is
+        // selected or not fully visible to the tile
+        float* pen = (float*)(smem + buf * C::STAGE + C::KBYTES + C::VBYTES);
+        const int h = tid >> 5, kk = tid & 31;
+        const int rho = 32 * (kk >> 4) + 8 * ((kk & 15) >> 2) + 4 * h + (kk & 3);
+        const int J = (it - T) * kChunk + rho;
+        const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
+        pen[tid] = ok ? 7.f : -INFINITY;
+      }
+    };
+
+    // issue the loads of step it into stage buf (DMA: straight to LDS)
+    auto load_step = [&](int buf, int it, int p) {
       if (it < T) {
         const int j0 = p * kTile;
         if constexpr (AM == kContig) {
           const uint64_t o = (uint64_t)j0 * rowstride;
           const uint64_t left = kvbytes > o ? kvbytes - o : 0;
           const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
+          if constexpr (C::DMA) {
+            dma_tile(buf, rk, rv);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bld8<DT>(kst[i], rk, voff_k[i], 0);
-            bld8<DT>(vst[i], rv, voff_v[i], 0);
+            for (int i = 0; i < 4; ++i) {
+              bld8<DT>(kst[i], rk, voff_k[i], 0);
+              bld8<DT>(vst[i], rv, voff_v[i], 0);
+            }
           }
         } else if constexpr (AM == kPagedTile) {
           const int pg = j0 / g.page_size;
@@ -380,26 +486,31 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             slot0 = 0;
           }
           const uint64_t o = (uint64_t)slot0 * rowstride;
-          const uint64_t left = kvbytes > o ? kvbytes - o : 0;
+          // rows past the end of the request read as zero: the range stops there
+          const uint64_t tail = (uint64_t)max(0, c.L - 1 - j0) * rowstride + C::ROWB;
+          const uint64_t left = min(kvbytes > o ? kvbytes - o : (uint64_t)0, tail);
           const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
+          if constexpr (C::DMA) {
+            dma_tile(buf, rk, rv);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bld8<DT>(kst[i], rk, voff_k[i], 0);
-            bld8<DT>(vst[i], rv, voff_v[i], 0);
-          }
-          if (j0 + kTile > c.L) {  // the request's last tile: slots past its end may hold anything
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (j0 + 4 * vq + i >= c.L) zero8<DT>(vst[i]);
+            for (int i = 0; i < 4; ++i) {
+              bld8<DT>(kst[i], rk, voff_k[i], 0);
+              bld8<DT>(vst[i], rv, voff_v[i], 0);
+            }
           }
         } else {
           const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, kvbytes), rv = make_rsrc(vbase, kvbytes);
+          if constexpr (C::DMA) {
+            dma_tile_rows(buf, j0, rk, rv);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int jk = min(j0 + kr + 16 * i, c.L - 1);
-            const int jv = min(j0 + 4 * vq + i, c.L - 1);
-            bld8<DT>(kst[i], rk, paged_off(g, c, jk, rowstride, err) + kc * EB, 0);
-            bld8<DT>(vst[i], rv, paged_off(g, c, jv, rowstride, err) + vc * EB, 0);
+            for (int i = 0; i < 4; ++i) {
+              const int jk = min(j0 + kr + 16 * i, c.L - 1);
+              const int jv = min(j0 + 4 * vq + i, c.L - 1);
+              bld8<DT>(kst[i], rk, paged_off(g, c, jk, rowstride, err) + kc * EB, 0);
+              bld8<DT>(vst[i], rv, paged_off(g, c, jv, rowstride, err) + vc * EB, 0);
+            }
           }
         }
       } else {
@@ -407,59 +518,91 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
         const uint64_t left = mbytes > o ? mbytes - o : 0;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kmbase + o, left), rv = make_rsrc(vmbase + o, left);
+        if constexpr (C::DMA) {
+          dma_tile(buf, rk, rv);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bld8<DT>(kst[i], rk, voff_k[i], 0);
-          bld8<DT>(vst[i], rv, voff_v[i], 0);
+          for (int i = 0; i < 4; ++i) {
+            bld8<DT>(kst[i], rk, voff_k[i], 0);
+            bld8<DT>(vst[i], rv, voff_v[i], 0);
+          }
         }
       }
+      if constexpr (C::DMA) write_pen(buf, it);
     };
 
+    // fp32 only: registers -> LDS (K rows padded, V transposed)
     auto store_step = [&](int buf, int it) {
-      char* ks = smem + buf * C::STAGE;
-      char* vt = ks + C::KBYTES;
+      if constexpr (!C::DMA) {
+        char* ks = smem + buf * C::STAGE;
+        char* vt = ks + C::KBYTES;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        char* dst = ks + (kr + 16 * i) * C::KPITCH + kc * EB;
-        if constexpr (DT == kBF16)
-          *(uint4*)dst = make_uint4(kst[i].w[0], kst[i].w[1], kst[i].w[2], kst[i].w[3]);
-        else if constexpr (DT == kE4M3)
-          *(uint2*)dst = make_uint2(kst[i].w[0], kst[i].w[1]);
-        else {
+        for (int i = 0; i < 4; ++i) {
+          char* dst = ks + (kr + 16 * i) * C::KPITCH + kc * EB;
           ((uint4*)dst)[0] = make_uint4(kst[i].w[0], kst[i].w[1], kst[i].w[2], kst[i].w[3]);
           ((uint4*)dst)[1] = make_uint4(kst[i].w[4], kst[i].w[5], kst[i].w[6], kst[i].w[7]);
         }
-      }
-      // V^T: row n = vc + e receives keys 4vq..4vq+3 at their permuted position
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        char* rowp = vt + (vc + e) * C::VPITCH;
-        if constexpr (DT == kBF16) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t lo = __builtin_amdgcn_perm(vst[1].w[e >> 1], vst[0].w[e >> 1], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(vst[3].w[e >> 1], vst[2].w[e >> 1], sel);
-          *(uint2*)(rowp + vpos * 2) = make_uint2(lo, hi);
-        } else if constexpr (DT == kE4M3) {
-          const int b = e & 3;
-          const uint32_t sel = 0x0c0c0400u | (uint32_t)b | ((uint32_t)b << 8);
-          const uint32_t lo = __builtin_amdgcn_perm(vst[1].w[e >> 2], vst[0].w[e >> 2], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(vst[3].w[e >> 2], vst[2].w[e >> 2], sel);
-          *(uint32_t*)(rowp + vpos) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-        } else {
+        for (int e = 0; e < 8; ++e) {
+          char* rowp = vt + (vc + e) * C::VPITCH;
 #pragma unroll
           for (int i = 0; i < 4; ++i) *(uint32_t*)(rowp + vt_pos<KPL>(4 * vq + i) * 4) = el<DT>(vst[i], e);
         }
+        write_pen(buf, it);
       }
-      if (it >= T && tid < 64) {
-        // logit offset of each register of a correction step, per lane half:
-        // + 7 (ln 128 in log2 units) where the block is corrected, -inf where it is
-        // selected or not fully visible to the tile
-        float* pen = (float*)(vt + C::VBYTES);
-        const int h = tid >> 5, k = tid & 31;
-        const int rho = 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * h + (k & 3);
-        const int J = (it - T) * kChunk + rho;
-        const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
-        pen[tid] = ok ? 7.f : -INFINITY;
+    };
+
+    // MFMA A operand m of logit tile jt (K rows) from stage buffer ks
+    auto k_op = [&](const char* ks, int jt, int m) -> Op {
+      const int rr = jt * 32 + col;
+      if constexpr (DT == kBF16) {
+        const char* rp = ks + rr * C::ROWB;
+        return __builtin_bit_cast(bf16x8, *(const uint4*)(rp + (((2 * m + half) ^ swz_k<DT>(rr)) << 4)));
+      } else if constexpr (DT == kE4M3) {
+        const char* rp = ks + rr * C::ROWB;
+        const int c0 = 4 * m + 2 * half, sw = swz_k<DT>(rr);
+        const uint4 a = *(const uint4*)(rp + ((c0 ^ sw) << 4));
+        const uint4 b = *(const uint4*)(rp + (((c0 + 1) ^ sw) << 4));
+        i32x8 r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        return r;
+      } else {
+        return lds_op<DT>(ks + rr * C::KPITCH + half * KPL * EB + m * 2 * KPL * EB);
+      }
+    };
+    // MFMA A operand m1 of output tile nt (V^T) from stage buffer
+    auto v_op = [&](const char* vs, int nt, int m1) -> Op {
+      if constexpr (DT == kBF16) {
+        // keys 16 m1 + 4 half + 0..3 and 16 m1 + 8 + 4 half + 0..3 of column
+        // nt*32 + lane%32, by two transpose reads of 4 rows x 16 columns
+        const int k16 = lane & 15;
+        const int colb = nt * 32 + 16 * ((lane >> 4) & 1) + 4 * (k16 & 3);
+        const int r1 = 16 * m1 + 4 * half + (k16 >> 2), r2 = r1 + 8;
+        const char* a1 = vs + r1 * C::ROWB + (((colb >> 3) ^ swz_v<DT>(r1)) << 4) + (colb & 7) * 2;
+        const char* a2 = vs + r2 * C::ROWB + (((colb >> 3) ^ swz_v<DT>(r2)) << 4) + (colb & 7) * 2;
+        const i16x4 x = lds_tr16(a1);
+        const i16x4 y = lds_tr16(a2);
+        const i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        return __builtin_bit_cast(bf16x8, z);
+      } else if constexpr (DT == kE4M3) {
+        // 32 keys of column nt*32 + lane%32 in the register order of P: read t
+        // (0..3) gives keys 16 t + 8 (i/4) + 4 half + i%4, i = 0..7
+        const int k16 = lane & 15;
+        const int colb = nt * 32 + 16 * ((lane >> 4) & 1) + 8 * (k16 & 1);
+        const int i = k16 >> 1;
+        i32x8 r;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int row = 16 * tt + 8 * (i >> 2) + 4 * half + (i & 3);
+          const char* a = vs + row * C::ROWB + (((colb >> 4) ^ swz_v<DT>(row)) << 4) + (colb & 15);
+          const i32x2 w = lds_tr8(a);
+          r[2 * tt] = w[0];
+          r[2 * tt + 1] = w[1];
+        }
+        return r;
+      } else {
+        return lds_op<DT>(vs + (nt * 32 + col) * C::VPITCH + half * KPL * EB + m1 * 2 * KPL * EB);
       }
     };
 
@@ -469,16 +612,17 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     int cur_tile = 0;
     if (cur < it1) {
       cur_tile = cur < T ? tile_of(cur) : 0;
-      load_step(cur, cur_tile);
+      load_step(0, cur, cur_tile);
       store_step(0, cur);
     }
+    if constexpr (C::DMA) wait_vmem();
     __syncthreads();
     while (cur < it1) {
       const int nxt = next_step(cur + 1);
       int nxt_tile = 0;
       if (nxt < it1) {
         nxt_tile = nxt < T ? tile_of(nxt) : 0;
-        load_step(nxt, nxt_tile);
+        load_step(buf ^ 1, nxt, nxt_tile);
       }
       const char* ks = smem + buf * C::STAGE;
       const char* vt = ks + C::KBYTES;
@@ -487,9 +631,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         sacc[jt] = f32x16{};
-        const char* arow = ks + (jt * 32 + col) * C::KPITCH + half * KPL * EB;
 #pragma unroll
-        for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(lds_op<DT>(arow + m * 2 * KPL * EB), qf[m], sacc[jt]);
+        for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(k_op(ks, jt, m), qf[m], sacc[jt]);
       }
       // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
       float m_step;
@@ -589,12 +732,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       l_i += psum;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const char* arow = vt + (nt * 32 + col) * C::VPITCH + half * KPL * EB;
 #pragma unroll
-        for (int m1 = 0; m1 < C::NM1; ++m1)
-          oacc[nt] = mma<DT>(lds_op<DT>(arow + m1 * 2 * KPL * EB), pf[m1], oacc[nt]);
+        for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
       }
       if (nxt < it1) store_step(buf ^ 1, nxt);
+      if constexpr (C::DMA) wait_vmem();
       __syncthreads();
       buf ^= 1;
       cur = nxt;
@@ -701,7 +843,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
     L += wgt[u] * ml[kRows + r];
   }
   const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
-  const float inv = L > 0.f ? cvs / L : NAN;
+  const float inv = cvs / L;
   const int64_t prow = c.I * kRows + r;
   const int pos = (int)(prow >> g.log2g);
   const int head = c.h * g.g + (int)(prow & (g.g - 1));
