@@ -37,6 +37,13 @@ def dense_flops(lengths, hq):
     return float(sum(2.0 * D * hq * L * (L + 1) for L in lengths))
 
 
+def algorithmic_bytes(batch):
+    """Least HBM bytes one attention launch must move: Q and O once, K and V once."""
+    eb = {"bf16": 2, "e4m3": 1, "f32": 4}[batch.dtype]
+    ob = 4 if batch.dtype == "f32" else 2
+    return float(batch.total * batch.hq * D * (eb + ob) + 2 * batch.total * batch.hkv * D * eb)
+
+
 def csr_work(lengths, hq, hkv, cu, idx, correction):
     """Algorithmic and executed attention FLOPs of a CSR (host arithmetic on the index).
 
@@ -80,6 +87,23 @@ def csr_work(lengths, hq, hkv, cu, idx, correction):
                 s += 1
     execd = 4.0 * D * 128 * 64 * steps
     return alg, execd, nsel_blocks / max(1, ncand)
+
+
+def recorded_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 byte counters,
+    only while the kernel source is the one that was profiled (else None)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "attn_traffic_128k_bf16.json")
+    src = os.path.join(ROOT, "block_sparse_long_mean_amd", "csrc", "attn.hip")
+    try:
+        rec = json.load(open(path))
+        cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("attn_hip_sha256") != cur:
+        return None
+    return float(rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"])
 
 
 def time_calls(fn, steps, warmup):
@@ -272,7 +296,9 @@ def main():
                    "sink_blocks": w.sink_blocks, "window_blocks": w.window_blocks,
                    "paged": bool(w.page_size), "mean_correction": True},
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (fp_sparse_attn)", "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": recorded_traffic(w.name), "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes": algorithmic_bytes(batch)},
         "extra": extra,
     }
     if not args.no_cpu_baseline:
