@@ -172,8 +172,9 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
   w.counts = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.scan_part = o; o = align256(o + (size_t)((hg.n_seg + 1023) / 1024 + 1) * 4);
   w.bits = o; o = align256(o + (size_t)hg.n_seg * hg.words * 4);
-  w.hist = o; o = align256(o + (size_t)kBuckets * 4);
-  w.cursor = o; o = align256(o + (size_t)kBuckets * 4);
+  w.work = o; o = align256(o + (size_t)hg.n_seg * 4);
+  w.wscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
+  w.uscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
   w.units = o; o = align256(o + (size_t)hg.n_seg * sp.umax * 8);
   w.part_o = o; o = align256(o + (sp.umax > 1 ? (size_t)hg.n_seg * sp.umax * kRows * kD * 4 : 0));
   w.part_ml = o; o = align256(o + (sp.umax > 1 ? (size_t)hg.n_seg * sp.umax * 2 * kRows * 4 : 0));

@@ -272,13 +272,28 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     voff_v[i] = (uint32_t)(4 * vq + i) * rowstride + vc * EB;
   }
 
+  // this workgroup's XCD (round-robin dispatch by workgroup id)
+  const int xcd = blockIdx.x % kXcds;
   for (;;) {
-    if (tid == 0) sh_unit = atomicAdd(&g.hdr->work_counter, 1);
+    if (tid == 0) {
+      // next unit of the own XCD's range, walked from its end; then the others'
+      int got = -1;
+      const int total = g.hdr->total_units;
+      for (int a = 0; a < kXcds && got < 0; ++a) {
+        const int x = (xcd + a) % kXcds;
+        const int lo = g.hdr->xcd_start[x];
+        const int hi = x + 1 < kXcds ? g.hdr->xcd_start[x + 1] : total;
+        if (hi <= lo || atomicAdd(&g.hdr->xcd_counter[x], 0) >= hi - lo) continue;
+        const int kk = atomicAdd(&g.hdr->xcd_counter[x], 1);
+        if (kk < hi - lo) got = hi - 1 - kk;
+      }
+      sh_unit = got;
+    }
     __syncthreads();
     // the unit id is wave-uniform; saying so keeps every value derived from it
     // (segment geometry, base addresses, buffer resources) in scalar registers
     const int u = __builtin_amdgcn_readfirstlane(sh_unit);
-    if (u >= g.hdr->total_units) break;
+    if (u < 0) break;
     const int2 ud = units[u];
     const Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
     const SegCoord c = seg_coord(g, un.s);

@@ -17,7 +17,7 @@ constexpr int kTile = 64;
 constexpr int kRows = 128;
 constexpr int kChunk = 64;        // blocks per correction chunk / padding unit of the means
 constexpr int kMaxBlocks = 8192;  // longest request: 8192 blocks = 1,048,576 tokens
-constexpr int kBuckets = 4096;    // work-size buckets of the scheduler
+constexpr int kXcds = 8;          // accelerator dies of an MI355X, each with its own L2
 
 enum Dtype : int32_t { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
 
@@ -28,9 +28,10 @@ constexpr int32_t kErrIdx = 2;
 // Workspace header words.
 struct WsHeader {
   int32_t err;
-  int32_t work_counter;
   int32_t total_units;
-  int32_t pad[61];
+  int32_t xcd_counter[kXcds];  // units taken from each XCD's range
+  int32_t xcd_start[kXcds];    // first unit of each XCD's range (the next range's start ends it)
+  int32_t pad[64 - 2 - 2 * kXcds];
 };
 
 // Everything a kernel needs to walk the batch.  Passed by value.
@@ -64,7 +65,7 @@ struct MeansLayout {
 
 // Layout of the workspace (byte offsets).
 struct WsLayout {
-  size_t hdr, seg_off, blk_base, counts, scan_part, bits, hist, cursor, units, part_o, part_ml, total;
+  size_t hdr, seg_off, blk_base, counts, scan_part, bits, work, wscan, uscan, units, part_o, part_ml, total;
   int32_t umax;           // largest split count of one segment
 };
 
