@@ -21,8 +21,9 @@
 // that register layout.  K/V tiles are gathered through the page table
 // ([V2] Eq. 22) with 8-element vector loads into registers one step ahead of
 // the MFMAs and written to the other half of a double-buffered LDS stage.
-// The persistent grid pulls work units, sorted by descending work on the
-// device, from an atomic counter.  bf16: v_mfma_f32_32x32x16_bf16; e4m3:
+// The persistent grid takes its work units from a list that the scheduler
+// cuts into work-balanced ranges, one per XCD, each served through an atomic
+// counter of its own.  bf16: v_mfma_f32_32x32x16_bf16; e4m3:
 // v_mfma_scale_f32_32x32x64_f8f6f4 with P quantised as e4m3(2^8 e^{s-m})
 // ([V2] Eq. 15); fp32: v_mfma_f32_32x32x2f32.
 #include "device_common.h"
@@ -130,6 +131,21 @@ __device__ __forceinline__ i32x2 lds_tr8(const char* p) {
 }
 // Wait for this wave's outstanding vector-memory loads (including LDS DMA).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Instruction-group ordering hints for the scheduler (one ordered chain per
+// block): a group of n instructions of the given class.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+
+// An empty use of a register value: it must be computed before this point.
+template <typename V>
+__device__ __forceinline__ void pin(const V& x) {
+  if constexpr (sizeof(V) == 4) {
+    asm volatile("" ::"v"(x));
+  } else if constexpr (sizeof(V) == 16) {
+    const uint4 w = __builtin_bit_cast(uint4, x);
+    asm volatile("" ::"v"(w.x), "v"(w.y), "v"(w.z), "v"(w.w));
+  }
+}
 
 // Position in a staged V^T row of key j (0..63) of the tile: keys are laid
 // out in the order in which each lane half holds the probabilities of the
@@ -248,7 +264,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   constexpr int EB = C::EB;
   extern __shared__ __align__(16) char smem[];
   uint32_t* selbits = (uint32_t*)(smem + 2 * C::STAGE);
-  __shared__ int sh_unit;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -272,28 +287,44 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     voff_v[i] = (uint32_t)(4 * vq + i) * rowstride + vc * EB;
   }
 
-  // this workgroup's XCD (round-robin dispatch by workgroup id)
-  const int xcd = blockIdx.x % kXcds;
-  for (;;) {
-    if (tid == 0) {
-      // next unit of the own XCD's range, walked from its end; then the others'
-      int got = -1;
-      const int total = g.hdr->total_units;
-      for (int a = 0; a < kXcds && got < 0; ++a) {
-        const int x = (xcd + a) % kXcds;
-        const int lo = g.hdr->xcd_start[x];
-        const int hi = x + 1 < kXcds ? g.hdr->xcd_start[x + 1] : total;
-        if (hi <= lo || atomicAdd(&g.hdr->xcd_counter[x], 0) >= hi - lo) continue;
-        const int kk = atomicAdd(&g.hdr->xcd_counter[x], 1);
-        if (kk < hi - lo) got = hi - 1 - kk;
-      }
-      sh_unit = got;
+  // Units come from the own XCD's range (workgroups are dispatched to XCDs
+  // round-robin by id), walked from its end through that range's counter;
+  // once it is exhausted, from the other ranges.  The atomic for the next unit
+  // is issued when a unit starts and its result is first needed when the
+  // unit ends, so its latency hides behind the unit's loads.
+  const int nx = gridDim.x % kXcds == 0 ? kXcds : 1;
+  const int xcd = blockIdx.x % nx;
+  auto range_of = [&](int x, int& lo, int& hi) {
+    lo = nx == kXcds ? g.hdr->xcd_start[x] : 0;
+    hi = nx == kXcds && x + 1 < kXcds ? g.hdr->xcd_start[x + 1] : g.hdr->total_units;
+  };
+  // the next unit from ranges x0, x0 + 1, ... (mod nx), given the own range's ticket
+  auto steal = [&](int x0) -> int {
+    for (int a = 0; a < nx; ++a) {
+      const int x = (x0 + a) % nx;
+      int lo, hi;
+      range_of(x, lo, hi);
+      if (hi <= lo || atomicAdd(&g.hdr->xcd_counter[x][0], 0) >= hi - lo) continue;
+      const int kk = atomicAdd(&g.hdr->xcd_counter[x][0], 1);
+      if (kk < hi - lo) return hi - 1 - kk;
     }
-    __syncthreads();
+    return -1;
+  };
+  int own_lo, own_hi;
+  range_of(xcd, own_lo, own_hi);
+  __shared__ int sh_unit;
+  if (tid == 0) {
+    const int kk = atomicAdd(&g.hdr->xcd_counter[xcd][0], 1);
+    sh_unit = kk < own_hi - own_lo ? own_hi - 1 - kk : steal(xcd + 1);
+  }
+  __syncthreads();
+  for (;;) {
     // the unit id is wave-uniform; saying so keeps every value derived from it
     // (segment geometry, base addresses, buffer resources) in scalar registers
     const int u = __builtin_amdgcn_readfirstlane(sh_unit);
     if (u < 0) break;
+    int ticket = 0;
+    if (tid == 0) ticket = atomicAdd(&g.hdr->xcd_counter[xcd][0], 1);
     const int2 ud = units[u];
     const Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
     const SegCoord c = seg_coord(g, un.s);
@@ -621,7 +652,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
-    // ---- mainloop: loads for step n+1 are in flight while step n computes
+    // ---- mainloop: loads for step n+1 are in flight while step n computes.
+    // Three kinds of step, each run by a loop of its own so that no step pays
+    // for another kind's work: listed tiles that reach past the first row's
+    // position (causal mask), then the other listed tiles, then correction
+    // chunks.  The listed tiles are visited in descending order, so the masked
+    // ones come first.
     int cur = next_step(it0);
     int buf = 0;
     int cur_tile = 0;
@@ -632,7 +668,16 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     }
     if constexpr (C::DMA) wait_vmem();
     __syncthreads();
-    while (cur < it1) {
+
+    // Output rescaling is deferred until a row's max exceeds the max that its
+    // accumulators are scaled to by more than 2^kTau (bf16 / fp32: exact up
+    // to rounding, probabilities stay below 2^8).  e4m3 quantises P against
+    // the running max itself (Eq. 15), so there kTau is 0.
+    constexpr float kTau = DT == kE4M3 ? 0.f : 8.f;
+    bool fresh = true;  // nothing accumulated yet: the first max needs no rescale
+
+    auto run_step = [&](auto kind_tag) {
+      constexpr int KIND = decltype(kind_tag)::value;  // 0 masked tile, 1 tile, 2 correction chunk
       const int nxt = next_step(cur + 1);
       int nxt_tile = 0;
       if (nxt < it1) {
@@ -642,6 +687,144 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       const char* ks = smem + buf * C::STAGE;
       const char* vt = ks + C::KBYTES;
 
+      if constexpr (DT == kBF16) {
+        // Software-scheduled step.  The MFMA sequence is S^T of keys 0-31 and
+        // 32-63 (8 MFMAs each), then O^T += V^T P^T for keys 0-31 and 32-63
+        // (8 each).  Each MFMA slot (closed by a scheduling fence) also issues
+        // the LDS reads of a later MFMA's operand (K four ahead, V^T two
+        // ahead) and a piece of the VALU work of a softmax half: that of
+        // keys 0-31 under the S^T MFMAs of keys 32-63, that of keys 32-63
+        // under the P V MFMAs of keys 0-31.  Only the rare rescale of the
+        // accumulators is a branch.
+        const f32x4* penp = (const f32x4*)(vt + C::VBYTES) + half * 8;
+        const int lim = pos - cur_tile * kTile - 4 * half;  // masked steps: key j visible iff j <= lim
+        f32x16 s0 = {}, s1 = {};
+        f32x4 pv[4];
+        Op ka[4], va[2], p0[2], p1[2];
+        float mh = 0.f, m_new = 0.f, m_use = 0.f, resc = 1.f, psum = 0.f;
+        bool need = false;
+
+        // one piece (0..7) of the softmax of a 32-key half held in sv
+        auto soft_piece = [&](f32x16& sv, int jt, int piece, Op* ph) {
+          if (piece == 0) {
+            if constexpr (KIND == 0) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sv[r] = -INFINITY;
+            }
+            if constexpr (KIND == 2) {
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = fmaf(sv[4 * r4 + e], sl, pv[r4][e]);
+            }
+            float a = fmaxf(sv[0], fmaxf(sv[1], sv[2]));
+            float b = fmaxf(sv[8], fmaxf(sv[9], sv[10]));
+            a = fmaxf(a, fmaxf(sv[3], sv[4]));
+            b = fmaxf(b, fmaxf(sv[11], sv[12]));
+            a = fmaxf(a, fmaxf(sv[5], sv[6]));
+            b = fmaxf(b, fmaxf(sv[13], sv[14]));
+            a = fmaxf(a, fmaxf(sv[7], b));
+            mh = fmaxf(a, sv[15]);
+            pin(mh);
+          } else if (piece == 1) {
+            // the other lane half holds the same query row: swap halves and combine
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
+                                                             __builtin_bit_cast(uint32_t, mh), false, false);
+            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+            const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
+            need = __any(m_half > m_i + kTau);
+            m_new = need ? fmaxf(m_i, m_half) : m_i;
+            m_use = m_new == -INFINITY ? 0.f : m_new;
+            resc = __builtin_amdgcn_exp2f(m_i - m_use);
+            pin(m_use);
+            pin(resc);
+          } else if (piece < 6) {
+            const int r0 = (piece - 2) * 4;
+#pragma unroll
+            for (int r = r0; r < r0 + 4; ++r) {
+              sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
+              pin(sv[r]);
+            }
+          } else {
+            // bf16 P; the denominator sums the rounded P that the numerator uses
+            const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+            const int q2 = piece - 6;
+            bf16x8 bv;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pr = {static_cast<__bf16>(sv[8 * q2 + e]), static_cast<__bf16>(sv[8 * q2 + e + 1])};
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+              bv[e] = pr[0];
+              bv[e + 1] = pr[1];
+            }
+            ph[q2] = bv;
+            pin(bv);
+            pin(psum);
+          }
+        };
+        auto commit = [&]() {
+          l_i = fmaf(l_i, resc, psum);
+          m_i = m_new;
+          psum = 0.f;
+        };
+        auto rescale = [&]() {
+          if (need && !fresh) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          }
+          fresh = false;
+        };
+
+        // S^T, keys 0-31; pen of keys 0-31 read in slots 4-7 (correction steps)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ka[i] = k_op(ks, 0, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const Op a = ka[i & 3];
+          ka[i & 3] = k_op(ks, (i + 4) >> 3, (i + 4) & 7);
+          if (KIND == 2 && i >= 4) pv[i - 4] = penp[i - 4];
+          s0 = mma<DT>(a, qf[i], s0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // S^T, keys 32-63, with the softmax of keys 0-31
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const Op a = ka[i & 3];
+          if (i < 4) ka[i & 3] = k_op(ks, 1, i + 4);
+          if (i >= 6) va[i - 6] = v_op(vt, 0, i - 6);
+          s1 = mma<DT>(a, qf[i], s1);
+          soft_piece(s0, 0, i, p0);
+          if (KIND == 2 && i == 7) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) pv[r4] = penp[4 + r4];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        commit();
+        rescale();
+        // P V, keys 0-31, with the softmax of keys 32-63
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const Op a = va[i & 1];
+          va[i & 1] = v_op(vt, (i + 2) >> 1 & 3, (i + 2 < 8) ? ((i + 2) & 1) : 2 + (i & 1));
+          oacc[i >> 1] = mma<DT>(a, p0[i & 1], oacc[i >> 1]);
+          soft_piece(s1, 1, i, p1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        commit();
+        rescale();
+        // P V, keys 32-63
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const Op a = va[i & 1];
+          if (i + 2 < 8) va[i & 1] = v_op(vt, (i + 2) >> 1, 2 + (i & 1));
+          oacc[i >> 1] = mma<DT>(a, p1[i & 1], oacc[i >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
       f32x16 sacc[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -649,106 +832,209 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
         for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(k_op(ks, jt, m), qf[m], sacc[jt]);
       }
-      // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
-      float m_step;
-      const bool chunk = cur >= T;
-      if (!chunk) {
-        const int kbase = cur_tile * kTile;
-        if (kbase + kTile - 1 > t.t0) {  // the tile reaches past some row's position
-          const int lim = pos - kbase - 4 * half;  // key j visible iff j <= pos - kbase
+      if constexpr (DT == kE4M3) {
+        // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
+        float mx;
+        if constexpr (KIND == 0) {
+          const int lim = pos - cur_tile * kTile - 4 * half;  // key j visible iff j <= pos - 64 p
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sacc[jt][r] = -INFINITY;
         }
-        float mraw = -INFINITY;
+        if constexpr (KIND == 2) {
+          // logit offsets of the step's pooled means (+7, or -inf where masked)
+          const f32x4* pen = (const f32x4*)(vt + C::VBYTES) + half * 8;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+          for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) mraw = fmaxf(mraw, fmaxf(sacc[jt][r], sacc[jt][r + 1]));
-        mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
-        m_step = mraw * sl;
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 pv = pen[jt * 4 + r4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sacc[jt][4 * r4 + e] = fmaf(sacc[jt][4 * r4 + e], sl, pv[e]);
+            }
+        }
+        {
+          // two chains of three-input maxima over the 32 logits
+          float a = fmaxf(sacc[0][0], fmaxf(sacc[0][1], sacc[0][2]));
+          float b = fmaxf(sacc[1][0], fmaxf(sacc[1][1], sacc[1][2]));
+#pragma unroll
+          for (int r = 3; r < 15; r += 2) {
+            a = fmaxf(a, fmaxf(sacc[0][r], sacc[0][r + 1]));
+            b = fmaxf(b, fmaxf(sacc[1][r], sacc[1][r + 1]));
+          }
+          a = fmaxf(a, fmaxf(sacc[0][15], b));
+          mx = fmaxf(sacc[1][15], a);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // tile steps hold raw dot products (sl > 0); chunk steps are already scaled
+        const float m_step = KIND == 2 ? mx : mx * sl;
+        if (fresh) {
+          m_i = m_step;
+          fresh = false;
+        } else if (__any(m_step > m_i + kTau)) {
+          const float m_new = fmaxf(m_i, m_step);
+          const float resc = __builtin_amdgcn_exp2f(m_i - (m_new == -INFINITY ? 0.f : m_new));
+          l_i *= resc;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          m_i = m_new;
+        }
+        const float m_use = m_i == -INFINITY ? 0.f : m_i;
+        if constexpr (KIND != 2) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], sl, kOff - m_use));
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(sacc[jt][r] + (kOff - m_use));
+        }
+
+        // P^T as the B operands of O^T += V^T P^T
+        Op pf[C::NM1];
+        if constexpr (DT == kBF16) {
+          // the denominator sums the bf16-rounded P that the numerator uses
+          const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+          float psum = 0.f;
+#pragma unroll
+          for (int m1 = 0; m1 < 4; ++m1) {
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pr = {static_cast<__bf16>(sacc[m1 >> 1][8 * (m1 & 1) + e]),
+                                 static_cast<__bf16>(sacc[m1 >> 1][8 * (m1 & 1) + e + 1])};
+              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+              b[e] = pr[0];
+              b[e + 1] = pr[1];
+            }
+            pf[m1] = b;
+          }
+          l_i += psum;
+        } else if constexpr (DT == kE4M3) {
+          float psum = 0.f;
+          i32x8 b;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int jt = w >> 2, r = (w & 3) * 4;
+            const uint32_t word = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]) |
+                                  (f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]) << 16);
+            const f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P (Eq. 15)
+            psum += (back[0] + back[1]) + (back[2] + back[3]);
+            b[w] = (int)word;
+          }
+          pf[0] = b;
+          l_i += psum;
+        } else {
+          float psum = 0.f;
+#pragma unroll
+          for (int m1 = 0; m1 < 32; ++m1) {
+            const float pv = sacc[m1 >> 4][m1 & 15];
+            psum += pv;
+            pf[m1] = pv;
+          }
+          l_i += psum;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+          for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
+        }
       } else {
-        const f32x4* pen = (const f32x4*)(vt + C::VBYTES) + half * 8;
-        float mx = -INFINITY;
+        // Two halves of 32 keys (logit tile jt), each an online-softmax update
+        // of its own.  The VALU work of half 0 overlaps the MFMAs of half 1's
+        // logits, that of half 1 overlaps the P V MFMAs of half 0: the rescale
+        // decision is taken without a branch, and only the (rare) rescale of
+        // the accumulators is conditional.
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int jt = 0; jt < 2; ++jt) {
+          f32x16& sv = sacc[jt];
+          if constexpr (KIND == 0) {
+            const int lim = pos - cur_tile * kTile - 4 * half;  // key j visible iff j <= pos - 64 p
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 pv = pen[jt * 4 + r4];
+            for (int r = 0; r < 16; ++r)
+              if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sv[r] = -INFINITY;
+          }
+          if constexpr (KIND == 2) {
+            const f32x4* pen = (const f32x4*)(vt + C::VBYTES) + half * 8 + jt * 4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float x = fmaf(sacc[jt][4 * r4 + e], sl, pv[e]);
-              sacc[jt][4 * r4 + e] = x;
-              mx = fmaxf(mx, x);
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 pv = pen[r4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = fmaf(sv[4 * r4 + e], sl, pv[e]);
             }
           }
-        m_step = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      }
-      const float m_new = fmaxf(m_i, m_step);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      if (__any(m_new > m_i)) {
-        const float resc = __builtin_amdgcn_exp2f(m_i - m_use);
-        l_i *= resc;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
-      }
-      m_i = m_new;
-      if (!chunk) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[jt][r], sl, kOff - m_use));
-      } else {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[jt][r] = __builtin_amdgcn_exp2f(sacc[jt][r] + (kOff - m_use));
-      }
-
-      // P^T as the B operands of O^T += V^T P^T
-      float psum = 0.f;
-      Op pf[C::NM1];
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int m1 = 0; m1 < 4; ++m1) {
-          bf16x8 b;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pv = sacc[m1 >> 1][8 * (m1 & 1) + e];
-            psum += pv;
-            b[e] = static_cast<__bf16>(pv);
+          float a = fmaxf(sv[0], fmaxf(sv[1], sv[2]));
+          float b = fmaxf(sv[8], fmaxf(sv[9], sv[10]));
+          a = fmaxf(a, fmaxf(sv[3], sv[4]));
+          b = fmaxf(b, fmaxf(sv[11], sv[12]));
+          a = fmaxf(a, fmaxf(sv[5], sv[6]));
+          b = fmaxf(b, fmaxf(sv[13], sv[14]));
+          a = fmaxf(a, fmaxf(sv[7], b));
+          float mh = fmaxf(a, sv[15]);
+          {
+            // the other lane half holds the same query row: swap halves and combine
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
+                                                             __builtin_bit_cast(uint32_t, mh), false, false);
+            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
           }
-          pf[m1] = b;
-        }
-      } else if constexpr (DT == kE4M3) {
-        i32x8 b;
+          const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
+          const bool need = __any(m_half > m_i + kTau);
+          const float m_new = need ? fmaxf(m_i, m_half) : m_i;
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float resc = __builtin_amdgcn_exp2f(m_i - m_use);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int jt = w >> 2, r = (w & 3) * 4;
-          const uint32_t word = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]) |
-                                (f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]) << 16);
-          const f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P (Eq. 15)
-          psum += (back[0] + back[1]) + (back[2] + back[3]);
-          b[w] = (int)word;
-        }
-        pf[0] = b;
-      } else {
+          for (int r = 0; r < 16; ++r)
+            sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
+          Op ph[C::NM1 / 2];
+          float psum = 0.f;
+          if constexpr (DT == kBF16) {
+            // the denominator sums the bf16-rounded P that the numerator uses
+            const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-        for (int m1 = 0; m1 < 32; ++m1) {
-          const float pv = sacc[m1 >> 4][m1 & 15];
-          psum += pv;
-          pf[m1] = pv;
+            for (int q2 = 0; q2 < 2; ++q2) {
+              bf16x8 bv;
+#pragma unroll
+              for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pr = {static_cast<__bf16>(sv[8 * q2 + e]), static_cast<__bf16>(sv[8 * q2 + e + 1])};
+                psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
+                bv[e] = pr[0];
+                bv[e + 1] = pr[1];
+              }
+              ph[q2] = bv;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              psum += sv[r];
+              ph[r] = sv[r];
+            }
+          }
+          l_i = fmaf(l_i, resc, psum);
+          m_i = m_new;
+          // P is complete here, before the rescale branch, so that its VALU
+          // work shares a block with (and overlaps) the preceding MFMAs
+#pragma unroll
+          for (int q2 = 0; q2 < C::NM1 / 2; ++q2) pin(ph[q2]);
+          if (need && !fresh) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          }
+          fresh = false;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int q2 = 0; q2 < C::NM1 / 2; ++q2)
+              oacc[nt] = mma<DT>(v_op(vt, nt, jt * (C::NM1 / 2) + q2), ph[q2], oacc[nt]);
         }
       }
-      l_i += psum;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-        for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
       }
       if (nxt < it1) store_step(buf ^ 1, nxt);
       if constexpr (C::DMA) wait_vmem();
@@ -756,11 +1042,20 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       buf ^= 1;
       cur = nxt;
       cur_tile = nxt_tile;
+    };
+    using KMasked = std::integral_constant<int, 0>;
+    using KTile = std::integral_constant<int, 1>;
+    using KChunk = std::integral_constant<int, 2>;
+    while (cur < it1 && cur < T && cur_tile * kTile + kTile - 1 > t.t0) run_step(KMasked{});
+    while (cur < it1 && cur < T) run_step(KTile{});
+    if constexpr (!DENSE) {
+      while (cur < it1) run_step(KChunk{});
     }
 
     // ---- epilogue: results as floats; a unit that saw malformed input stores
     // NaN bit patterns instead (a separate branch, so no float select is involved)
     if (err) atomicOr(&g.hdr->err, (int)err);
+    if (tid == 0) sh_unit = ticket < own_hi - own_lo ? own_hi - 1 - ticket : steal(xcd + 1);
     const bool bad = __syncthreads_or(err != 0) != 0;
     const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
     if (un.nsplit == 1) {

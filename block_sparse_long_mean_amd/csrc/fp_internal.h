@@ -29,9 +29,11 @@ constexpr int32_t kErrIdx = 2;
 struct WsHeader {
   int32_t err;
   int32_t total_units;
-  int32_t xcd_counter[kXcds];  // units taken from each XCD's range
   int32_t xcd_start[kXcds];    // first unit of each XCD's range (the next range's start ends it)
-  int32_t pad[64 - 2 - 2 * kXcds];
+  int32_t pad[32 - 2 - kXcds];
+  // units taken from each XCD's range, one 128-byte line apiece: atomics on
+  // one line are serialised by the memory-side atomic unit
+  int32_t xcd_counter[kXcds][32];
 };
 
 // Everything a kernel needs to walk the batch.  Passed by value.

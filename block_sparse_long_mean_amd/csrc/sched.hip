@@ -3,18 +3,19 @@
 // [V2] §3.3 "Sparsity-Aware Load Balancing": the cost of a query tile is its
 // step count W = T (listed tiles) + C (mean-correction chunks); splits are
 // always admitted, each split getting an equal share of the steps by count
-// (Eq. 18), and heavy work is issued first.
+// (Eq. 18).
 //
 // MI355X layout.  Each of the 8 XCDs has its own L2, and neighbouring query
 // tiles of one KV head share most of their key tiles (sink, window, diagonal,
 // the same clusters).  The segment list (ordered request, KV head, tile) is
 // therefore cut into 8 contiguous ranges of equal total work, range x served
 // by the workgroups of XCD x (workgroups are dispatched to XCDs round-robin by
-// id), each range walked from its end: later tiles carry more candidate
-// blocks and correction chunks, so this is close to heaviest-first while the
-// tiles in flight on one XCD stay neighbours.  A workgroup whose range is
-// exhausted takes units from the other ranges.  Units of a segment with U
-// splits are contiguous; outputs do not depend on which workgroup runs a unit
+// id) through that XCD's atomic counter, each range walked from its end:
+// later tiles carry more candidate blocks and correction chunks, so this is
+// close to heaviest-first while the tiles in flight on one XCD stay
+// neighbours.  A workgroup whose range is exhausted takes units from the
+// other ranges.  Units of a segment with U splits
+// are contiguous; outputs do not depend on which workgroup runs a unit
 // (splits are merged in split order).
 #include "device_common.h"
 
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void sched_place_kernel(Geo g, const int32_t* 
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = g.n_seg;
   const int64_t wtot = max(1, wscan[n]);
-  if (blockIdx.x == 0 && threadIdx.x < kXcds) g.hdr->xcd_counter[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kXcds) g.hdr->xcd_counter[threadIdx.x][0] = 0;
   if (s == 0) g.hdr->total_units = uscan[n];
   if (s >= n) return;
   const int x = (int)min<int64_t>(kXcds - 1, (int64_t)wscan[s] * kXcds / wtot);
