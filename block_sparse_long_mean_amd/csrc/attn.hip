@@ -77,6 +77,24 @@ __device__ __forceinline__ f32x16 mma(typename Tr<DT>::Op a, typename Tr<DT>::Op
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// bf16 staging of the pipelined mainloop: rows padded instead of swizzled, so
+// that every MFMA operand address is a per-lane base plus an immediate.
+// K rows take 272 bytes (17 slots of 16 B: the 16-lane passes of the
+// 128-bit operand reads, rows r..r+15 at one chunk, fall on distinct bank
+// groups), V rows 320 bytes (20 slots: the 4 rows x 64 bytes that a pass of
+// transpose reads touches fall on disjoint banks).  A DMA instruction fills
+// 64 consecutive slots; the lane of a pad slot fetches a duplicate chunk.
+struct PipeL {
+  static constexpr int KSL = 17, VSL = 20;            // 16-byte slots per K / V row
+  static constexpr int KP = 16 * KSL, VP = 16 * VSL;  // row pitches (bytes)
+  static constexpr int KB = 64 * KP, VB = 64 * VP;    // one staged tile
+  static constexpr int NK = 64 * KSL / 64, NV = 64 * VSL / 64;  // DMA instructions per tile
+  static constexpr int V0 = 0, V1 = VB, K0 = 2 * VB, K1 = 2 * VB + KB;
+  static constexpr int PEN = 2 * VB + 2 * KB;         // three 256-byte correction-offset tables
+  static constexpr int SEL = PEN + 3 * 256;
+  static constexpr int LDS = SEL + (kMaxBlocks / 32 + 8) * 4;
+};
+
 template <int DT>
 struct Cfg {
   static constexpr int EB = Tr<DT>::EB;
@@ -92,7 +110,8 @@ struct Cfg {
   static constexpr int VBYTES = DMA ? kTile * VPITCH : kD * VPITCH;
   static constexpr int PENBYTES = 2 * 32 * 4;    // correction-step logit offsets, per lane half
   static constexpr int STAGE = KBYTES + VBYTES + PENBYTES;
-  static constexpr int LDS = 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
+  static constexpr int SELOFF = DT == kBF16 ? PipeL::SEL : 2 * STAGE;  // selection bitmask of the unit
+  static constexpr int LDS = DT == kBF16 ? PipeL::LDS : 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
   static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
   static constexpr int NM1 = kTile / (2 * KPL);  // MFMAs per 32-column output tile
   static constexpr int WGS = DT == kF32 ? 1 : 2; // workgroups per CU
@@ -101,17 +120,17 @@ struct Cfg {
   static constexpr int NDMA = kTile / RPI / 4;   // DMA instructions per wave per K (or V) tile
 };
 
-// XOR swizzles of the 16-byte chunks of a staged row, chosen so that the
-// MFMA operand reads hit distinct LDS banks: K rows are read 16 rows at a
-// time at one chunk; V rows are read by the transpose loads 4 (bf16) or 8
-// (e4m3) rows at a time at one or two chunks.
+// e4m3 staging: XOR swizzles of the 16-byte chunks of a 128-byte row, chosen
+// so that the MFMA operand reads hit distinct LDS banks: K rows are read 16
+// rows at a time at two chunks; V rows are read by the transpose loads 8 rows
+// at a time at one or two chunks.
 template <int DT>
 __device__ __forceinline__ int swz_k(int r) {
-  return DT == kBF16 ? (r & 15) : ((r >> 1) & 7);
+  return (r >> 1) & 7;
 }
 template <int DT>
 __device__ __forceinline__ int swz_v(int r) {
-  return DT == kBF16 ? 4 * (r & 3) : 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+  return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -263,7 +282,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   constexpr int KPL = C::KPL;
   constexpr int EB = C::EB;
   extern __shared__ __align__(16) char smem[];
-  uint32_t* selbits = (uint32_t*)(smem + 2 * C::STAGE);
+  uint32_t* selbits = (uint32_t*)(smem + C::SELOFF);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -286,6 +305,27 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     voff_k[i] = (uint32_t)(kr + 16 * i) * rowstride + kc * EB;
     voff_v[i] = (uint32_t)(4 * vq + i) * rowstride + vc * EB;
   }
+
+  // bf16: per-lane byte offsets (within a 64-row tile of K or V rows) of the
+  // DMA instructions q = wave + 4 i: lane L fills slot 64 q + L of the padded
+  // tile, i.e. row (64 q + L) / slots-per-row, chunk (64 q + L) % slots-per-row
+  // (a pad slot repeats chunk 15 of its row)
+  uint32_t pdk[5], pdv[5];
+  if constexpr (DT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int sk = 64 * (wave + 4 * i) + lane, sv = sk;
+      const int rk = sk / PipeL::KSL, ck = min(sk - rk * PipeL::KSL, 15);
+      const int rv = sv / PipeL::VSL, cv = min(sv - rv * PipeL::VSL, 15);
+      pdk[i] = (uint32_t)rk * rowstride + (uint32_t)ck * 16;
+      pdv[i] = (uint32_t)rv * rowstride + (uint32_t)cv * 16;
+    }
+  }
+  // bf16 operand addresses relative to a staged tile: K row jt*32 + col, chunk
+  // 2 m + half; V^T rows for the transpose reads (see the operand builders)
+  const int k16 = lane & 15, g16 = (lane >> 4) & 1;
+  const int lane_k = col * PipeL::KP + half * 16;
+  const int lane_v = (4 * half + (k16 >> 2)) * PipeL::VP + (16 * g16 + 4 * (k16 & 3)) * 2;
 
   // Units come from the own XCD's range (workgroups are dispatched to XCDs
   // round-robin by id), walked from its end through that range's counter;
@@ -445,6 +485,315 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
+    // Output rescaling is deferred until a row's max exceeds the max that its
+    // accumulators are scaled to by more than 2^kTau (bf16 / fp32: exact up
+    // to rounding, probabilities stay below 2^8).  e4m3 quantises P against
+    // the running max itself (Eq. 15), so there kTau is 0.
+    constexpr float kTau = DT == kE4M3 ? 0.f : 8.f;
+    bool fresh = true;  // nothing accumulated yet: the first max needs no rescale
+
+    if constexpr (DT == kBF16) {
+      // ---- bf16 mainloop, software-pipelined across steps.
+      // MFMA groups of step n: A(n), B(n) = S^T of keys 0-31 / 32-63 (K(n)
+      // operands), C(n), D(n) = O^T += V^T P^T for keys 0-31 / 32-63 (V(n)).
+      // Iteration n issues D(n-1), B(n), C(n), A(n+1), 32 MFMA slots; the
+      // softmax of keys 0-31 of step n runs in small pieces under D(n-1) and
+      // B(n), that of keys 32-63 under C(n) and A(n+1), a few VALU
+      // instructions per MFMA.  One barrier per iteration, between B(n) and
+      // C(n): K(n+1) and V(n) (loaded one iteration earlier) become visible,
+      // K(n+2) and V(n+1) are loaded.  K tiles alternate between two buffers
+      // by step parity, V tiles likewise, correction offsets rotate through
+      // three tables.  The first iteration's D(-1) multiplies a copy of V(0)
+      // by P = 0 (adding exact zeros); the last iteration's A(n+1) is computed
+      // on stale data and not used.
+      using PL = PipeL;
+      auto kread = [&](const char* kb, int jt, int m) -> Op {
+        return __builtin_bit_cast(bf16x8, *(const uint4*)(kb + jt * 32 * PL::KP + m * 32));
+      };
+      // keys 16 m1 + 4 half + 0..3 and +8 of V^T row nt*32 + lane%32
+      auto vread = [&](const char* vb, int nt, int m1) -> Op {
+        const i16x4 x = lds_tr16(vb + m1 * 16 * PL::VP + nt * 64);
+        const i16x4 y = lds_tr16(vb + m1 * 16 * PL::VP + 8 * PL::VP + nt * 64);
+        const i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        return __builtin_bit_cast(bf16x8, z);
+      };
+      // DMA of the K (ISK) or V tile of step it into LDS at lds_off
+      auto dma_bf16 = [&](auto isk_tag, int lds_off, int it, int p) {
+        constexpr bool ISK = decltype(isk_tag)::value;
+        constexpr int NQ = ISK ? PL::NK : PL::NV, SPR = ISK ? PL::KSL : PL::VSL;
+        const char* base = ISK ? kbase : vbase;
+        const char* mb = ISK ? kmbase : vmbase;
+        __amdgpu_buffer_rsrc_t r;
+        bool rows = false;
+        int j0 = 0;
+        if (it < T) {
+          j0 = p * kTile;
+          if constexpr (AM == kContig) {
+            const uint64_t o = (uint64_t)j0 * rowstride;
+            r = make_rsrc(base + o, kvbytes > o ? kvbytes - o : 0);
+          } else if constexpr (AM == kPagedTile) {
+            const int pg = j0 / g.page_size;
+            const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+            int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
+            if (page < 0 || slot0 + kTile > g.num_slots) {
+              err |= kErrPage;
+              slot0 = 0;
+            }
+            const uint64_t o = (uint64_t)slot0 * rowstride;
+            const uint64_t tail = (uint64_t)max(0, c.L - 1 - j0) * rowstride + C::ROWB;
+            r = make_rsrc(base + o, min(kvbytes > o ? kvbytes - o : (uint64_t)0, tail));
+          } else {
+            r = make_rsrc(base, kvbytes);
+            rows = true;
+          }
+        } else {
+          const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
+          r = make_rsrc(mb + o, mbytes > o ? mbytes - o : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          const int q = wave + 4 * i;
+          if (i < 4 || q < NQ) {
+            uint32_t voff = ISK ? pdk[i] : pdv[i];
+            if constexpr (AM == kPagedAny) {
+              if (rows) {
+                // one page-table lookup per row; rows past the request read as zero
+                const int sl = 64 * q + lane, row = sl / SPR, cc = min(sl - row * SPR, 15);
+                const int j = j0 + row;
+                voff = j < c.L ? paged_off(g, c, j, rowstride, err) + (uint32_t)cc * 16 : 0xfffffff0u;
+              }
+            }
+            dma16(r, smem + lds_off + q * 1024, voff);
+          }
+        }
+      };
+      // correction offsets of step it (+7 where the block is corrected, -inf
+      // where selected or not fully visible) into table ps, by wave 0
+      auto pen_bf16 = [&](int ps, int it) {
+        if (it >= T && tid < 64) {
+          float* pen = (float*)(smem + PL::PEN + ps * 256);
+          const int h = tid >> 5, kk = tid & 31;
+          const int rho = 32 * (kk >> 4) + 8 * ((kk & 15) >> 2) + 4 * h + (kk & 3);
+          const int J = (it - T) * kChunk + rho;
+          const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
+          pen[tid] = ok ? 7.f : -INFINITY;
+        }
+      };
+
+      int cur = next_step(it0);
+      if (cur < it1) {
+        int cur_tile = cur < T ? tile_of(cur) : 0;
+        int nxt = next_step(cur + 1);
+        int nxt_tile = nxt < it1 && nxt < T ? tile_of(nxt) : 0;
+        int bk = 0, ps = 0;  // parity of step n; its correction table n % 3
+        // prologue: K(0), V(0), K(1) staged; A(0)
+        dma_bf16(std::true_type{}, PL::K0, cur, cur_tile);
+        pen_bf16(0, cur);
+        dma_bf16(std::false_type{}, PL::V0, cur, cur_tile);
+        dma_bf16(std::false_type{}, PL::V1, cur, cur_tile);  // read by D(-1), with P = 0
+        if (nxt < it1) {
+          dma_bf16(std::true_type{}, PL::K1, nxt, nxt_tile);
+          pen_bf16(1, nxt);
+        }
+        wait_vmem();
+        __syncthreads();
+
+        f32x16 s0 = {}, s1 = {};
+        Op p0[2], p1[2], ring[4];
+        p1[0] = p1[1] = p0[0] = p0[1] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        {
+          const char* kb = smem + PL::K0 + lane_k;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) ring[m] = kread(kb, 0, m);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const Op a = ring[m & 3];
+            if (m + 4 < 8) ring[m & 3] = kread(kb, 0, m + 4);
+            s0 = mma<DT>(a, qf[m], s0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // operands of D(-1): V(0) again, times P = 0
+          const char* vb = smem + PL::V1 + lane_v;
+#pragma unroll
+          for (int g2 = 0; g2 < 4; ++g2) ring[g2] = vread(vb, g2 >> 1, 2 + (g2 & 1));
+        }
+
+        // softmax state of the current half
+        float ma = 0.f, mh = 0.f, m_new = 0.f, m_use = 0.f, resc = 1.f, psum = 0.f;
+        bool need = false;
+        f32x4 pv[2];  // correction offsets of 8 registers, read one piece ahead
+        // piece k (0..15) of the softmax of a 32-key half sv (logit tile jt)
+        auto sub = [&](auto kind_tag, f32x16& sv, int jt, int k, Op* ph, const f32x4* penp) {
+          constexpr int KIND = decltype(kind_tag)::value;
+          if (k == 0) {
+            if constexpr (KIND == 2) {
+              pv[0] = penp[0];
+              pv[1] = penp[1];
+            }
+          } else if (k <= 2) {
+            const int r0 = (k - 1) * 8;
+            if constexpr (KIND == 0) {
+              const int lim = pos - cur_tile * kTile - 4 * half;  // key j visible iff j <= pos - 64 p
+#pragma unroll
+              for (int r = r0; r < r0 + 8; ++r)
+                if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sv[r] = -INFINITY;
+            }
+            if constexpr (KIND == 2) {
+#pragma unroll
+              for (int r = r0; r < r0 + 8; ++r) sv[r] = fmaf(sv[r], sl, pv[(r >> 2) & 1][r & 3]);
+              if (k == 1) {
+                pv[0] = penp[2];
+                pv[1] = penp[3];
+              }
+            }
+#pragma unroll
+            for (int r = r0; r < r0 + 8; ++r) pin(sv[r]);
+          } else if (k == 3) {
+            ma = fmaxf(sv[0], fmaxf(sv[1], sv[2]));
+            ma = fmaxf(ma, fmaxf(sv[3], sv[4]));
+            ma = fmaxf(ma, fmaxf(sv[5], sv[6]));
+            ma = fmaxf(ma, sv[7]);
+            pin(ma);
+          } else if (k == 4) {
+            float mb = fmaxf(sv[8], fmaxf(sv[9], sv[10]));
+            mb = fmaxf(mb, fmaxf(sv[11], sv[12]));
+            mb = fmaxf(mb, fmaxf(sv[13], sv[14]));
+            mh = fmaxf(ma, fmaxf(mb, sv[15]));
+            pin(mh);
+          } else if (k == 5) {
+            // the other lane half holds the same query row: swap halves and combine
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
+                                                             __builtin_bit_cast(uint32_t, mh), false, false);
+            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+            const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
+            need = __any(m_half > m_i + kTau);
+            m_new = need ? fmaxf(m_i, m_half) : m_i;
+            m_use = m_new == -INFINITY ? 0.f : m_new;
+            resc = __builtin_amdgcn_exp2f(m_i - m_use);
+            pin(m_use);
+            pin(resc);
+          } else if (k < 14) {
+            const int r0 = (k - 6) * 2;
+#pragma unroll
+            for (int r = r0; r < r0 + 2; ++r) {
+              sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
+              pin(sv[r]);
+            }
+          } else {
+            // bf16 P and the fp32 row sum (plain adds: they issue beside the
+            // MFMAs, where bf16 dot products would not)
+            const int q2 = k - 14;
+            bf16x8 bv;
+            float ps2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bv[e] = static_cast<__bf16>(sv[8 * q2 + e]);
+              ps2 += sv[8 * q2 + e];
+            }
+            psum += ps2;
+            ph[q2] = bv;
+            pin(bv);
+            pin(psum);
+          }
+        };
+        auto commit = [&]() {
+          l_i = fmaf(l_i, resc, psum);
+          m_i = m_new;
+          psum = 0.f;
+          if (need && !fresh) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          }
+          fresh = false;
+        };
+
+        auto iter = [&](auto kind_tag) {
+          const char* kbc = smem + (bk ? PL::K1 : PL::K0) + lane_k;  // K(n)
+          const char* kbn = smem + (bk ? PL::K0 : PL::K1) + lane_k;  // K(n+1)
+          const char* vbc = smem + (bk ? PL::V1 : PL::V0) + lane_v;  // V(n)
+          const char* vbp = smem + (bk ? PL::V0 : PL::V1) + lane_v;  // V(n-1)
+          const f32x4* penp = (const f32x4*)(smem + PL::PEN + ps * 256) + half * 8;
+          auto fetch = [&](int gs) -> Op {
+            if (gs < 8) return vread(vbp, gs >> 1, 2 + (gs & 1));
+            if (gs < 16) return kread(kbc, 1, gs - 8);
+            if (gs < 24) return vread(vbc, (gs - 16) >> 1, (gs - 16) & 1);
+            if (gs < 32) return kread(kbn, 0, gs - 24);
+            return vread(vbc, (gs - 32) >> 1, 2 + (gs & 1));
+          };
+          auto mfma_slot = [&](int gs, const Op a) {
+            if (gs < 8)
+              oacc[gs >> 1] = mma<DT>(a, p1[gs & 1], oacc[gs >> 1]);
+            else if (gs < 16)
+              s1 = mma<DT>(a, qf[gs - 8], s1);
+            else if (gs < 24)
+              oacc[(gs - 16) >> 1] = mma<DT>(a, p0[(gs - 16) & 1], oacc[(gs - 16) >> 1]);
+            else
+              s0 = mma<DT>(a, qf[gs - 24], s0);
+          };
+          // slots 0-15: D(n-1), B(n); softmax of keys 0-31
+          s1 = f32x16{};
+#pragma unroll
+          for (int gs = 0; gs < 16; ++gs) {
+            const Op a = ring[gs & 3];
+            if (gs + 4 < 16) ring[gs & 3] = fetch(gs + 4);
+            sub(kind_tag, s0, 0, gs, p0, penp);
+            mfma_slot(gs, a);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          commit();
+          // K(n+1), V(n) visible; K(n+2), V(n+1) loaded
+          wait_vmem();
+          __syncthreads();
+          int nxt2 = nxt, nxt2_tile = 0;
+          if (nxt < it1) {
+            nxt2 = next_step(nxt + 1);
+            if (nxt2 < it1 && nxt2 < T) nxt2_tile = tile_of(nxt2);
+          }
+          if (nxt2 < it1) {
+            dma_bf16(std::true_type{}, bk ? PL::K1 : PL::K0, nxt2, nxt2_tile);
+            pen_bf16(ps == 0 ? 2 : ps - 1, nxt2);
+          }
+          if (nxt < it1) dma_bf16(std::false_type{}, bk ? PL::V0 : PL::V1, nxt, nxt_tile);
+#pragma unroll
+          for (int gs = 16; gs < 20; ++gs) ring[gs & 3] = fetch(gs);
+          // slots 16-31: C(n), A(n+1); softmax of keys 32-63
+          s0 = f32x16{};
+#pragma unroll
+          for (int gs = 16; gs < 32; ++gs) {
+            const Op a = ring[gs & 3];
+            ring[gs & 3] = fetch(gs + 4);
+            sub(kind_tag, s1, 1, gs - 16, p1, penp + 4);
+            mfma_slot(gs, a);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          commit();
+          bk ^= 1;
+          ps = ps == 2 ? 0 : ps + 1;
+          cur = nxt;
+          cur_tile = nxt_tile;
+          nxt = nxt2;
+          nxt_tile = nxt2_tile;
+        };
+        while (cur < it1 && cur < T && cur_tile * kTile + kTile - 1 > t.t0) iter(std::integral_constant<int, 0>{});
+        while (cur < it1 && cur < T) iter(std::integral_constant<int, 1>{});
+        if constexpr (!DENSE) {
+          while (cur < it1) iter(std::integral_constant<int, 2>{});
+        }
+        // D of the last step (its V tile has the other parity)
+        {
+          const char* vb = smem + (bk ? PL::V0 : PL::V1) + lane_v;
+#pragma unroll
+          for (int gs = 0; gs < 8; ++gs) {
+            const Op a = ring[gs & 3];
+            if (gs + 4 < 8) ring[gs & 3] = vread(vb, (gs + 4) >> 1, 2 + (gs & 1));
+            oacc[gs >> 1] = mma<DT>(a, p1[gs & 1], oacc[gs >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    } else {
     // per-lane DMA offsets within a 64-row tile (bf16/e4m3): instruction q of
     // wave w fills rows 16w + RPI q + lane / CPR, chunk lane % CPR, which holds
     // the row's logical chunk (lane % CPR) ^ swizzle(row)
@@ -601,10 +950,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     // MFMA A operand m of logit tile jt (K rows) from stage buffer ks
     auto k_op = [&](const char* ks, int jt, int m) -> Op {
       const int rr = jt * 32 + col;
-      if constexpr (DT == kBF16) {
-        const char* rp = ks + rr * C::ROWB;
-        return __builtin_bit_cast(bf16x8, *(const uint4*)(rp + (((2 * m + half) ^ swz_k<DT>(rr)) << 4)));
-      } else if constexpr (DT == kE4M3) {
+      if constexpr (DT == kE4M3) {
         const char* rp = ks + rr * C::ROWB;
         const int c0 = 4 * m + 2 * half, sw = swz_k<DT>(rr);
         const uint4 a = *(const uint4*)(rp + ((c0 ^ sw) << 4));
@@ -619,19 +965,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     };
     // MFMA A operand m1 of output tile nt (V^T) from stage buffer
     auto v_op = [&](const char* vs, int nt, int m1) -> Op {
-      if constexpr (DT == kBF16) {
-        // keys 16 m1 + 4 half + 0..3 and 16 m1 + 8 + 4 half + 0..3 of column
-        // nt*32 + lane%32, by two transpose reads of 4 rows x 16 columns
-        const int k16 = lane & 15;
-        const int colb = nt * 32 + 16 * ((lane >> 4) & 1) + 4 * (k16 & 3);
-        const int r1 = 16 * m1 + 4 * half + (k16 >> 2), r2 = r1 + 8;
-        const char* a1 = vs + r1 * C::ROWB + (((colb >> 3) ^ swz_v<DT>(r1)) << 4) + (colb & 7) * 2;
-        const char* a2 = vs + r2 * C::ROWB + (((colb >> 3) ^ swz_v<DT>(r2)) << 4) + (colb & 7) * 2;
-        const i16x4 x = lds_tr16(a1);
-        const i16x4 y = lds_tr16(a2);
-        const i16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-        return __builtin_bit_cast(bf16x8, z);
-      } else if constexpr (DT == kE4M3) {
+      if constexpr (DT == kE4M3) {
         // 32 keys of column nt*32 + lane%32 in the register order of P: read t
         // (0..3) gives keys 16 t + 8 (i/4) + 4 half + i%4, i = 0..7
         const int k16 = lane & 15;
@@ -669,13 +1003,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if constexpr (C::DMA) wait_vmem();
     __syncthreads();
 
-    // Output rescaling is deferred until a row's max exceeds the max that its
-    // accumulators are scaled to by more than 2^kTau (bf16 / fp32: exact up
-    // to rounding, probabilities stay below 2^8).  e4m3 quantises P against
-    // the running max itself (Eq. 15), so there kTau is 0.
-    constexpr float kTau = DT == kE4M3 ? 0.f : 8.f;
-    bool fresh = true;  // nothing accumulated yet: the first max needs no rescale
-
     auto run_step = [&](auto kind_tag) {
       constexpr int KIND = decltype(kind_tag)::value;  // 0 masked tile, 1 tile, 2 correction chunk
       const int nxt = next_step(cur + 1);
@@ -687,144 +1014,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       const char* ks = smem + buf * C::STAGE;
       const char* vt = ks + C::KBYTES;
 
-      if constexpr (DT == kBF16) {
-        // Software-scheduled step.  The MFMA sequence is S^T of keys 0-31 and
-        // 32-63 (8 MFMAs each), then O^T += V^T P^T for keys 0-31 and 32-63
-        // (8 each).  Each MFMA slot (closed by a scheduling fence) also issues
-        // the LDS reads of a later MFMA's operand (K four ahead, V^T two
-        // ahead) and a piece of the VALU work of a softmax half: that of
-        // keys 0-31 under the S^T MFMAs of keys 32-63, that of keys 32-63
-        // under the P V MFMAs of keys 0-31.  Only the rare rescale of the
-        // accumulators is a branch.
-        const f32x4* penp = (const f32x4*)(vt + C::VBYTES) + half * 8;
-        const int lim = pos - cur_tile * kTile - 4 * half;  // masked steps: key j visible iff j <= lim
-        f32x16 s0 = {}, s1 = {};
-        f32x4 pv[4];
-        Op ka[4], va[2], p0[2], p1[2];
-        float mh = 0.f, m_new = 0.f, m_use = 0.f, resc = 1.f, psum = 0.f;
-        bool need = false;
-
-        // one piece (0..7) of the softmax of a 32-key half held in sv
-        auto soft_piece = [&](f32x16& sv, int jt, int piece, Op* ph) {
-          if (piece == 0) {
-            if constexpr (KIND == 0) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) sv[r] = -INFINITY;
-            }
-            if constexpr (KIND == 2) {
-#pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sv[4 * r4 + e] = fmaf(sv[4 * r4 + e], sl, pv[r4][e]);
-            }
-            float a = fmaxf(sv[0], fmaxf(sv[1], sv[2]));
-            float b = fmaxf(sv[8], fmaxf(sv[9], sv[10]));
-            a = fmaxf(a, fmaxf(sv[3], sv[4]));
-            b = fmaxf(b, fmaxf(sv[11], sv[12]));
-            a = fmaxf(a, fmaxf(sv[5], sv[6]));
-            b = fmaxf(b, fmaxf(sv[13], sv[14]));
-            a = fmaxf(a, fmaxf(sv[7], b));
-            mh = fmaxf(a, sv[15]);
-            pin(mh);
-          } else if (piece == 1) {
-            // the other lane half holds the same query row: swap halves and combine
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
-                                                             __builtin_bit_cast(uint32_t, mh), false, false);
-            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-            const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
-            need = __any(m_half > m_i + kTau);
-            m_new = need ? fmaxf(m_i, m_half) : m_i;
-            m_use = m_new == -INFINITY ? 0.f : m_new;
-            resc = __builtin_amdgcn_exp2f(m_i - m_use);
-            pin(m_use);
-            pin(resc);
-          } else if (piece < 6) {
-            const int r0 = (piece - 2) * 4;
-#pragma unroll
-            for (int r = r0; r < r0 + 4; ++r) {
-              sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
-              pin(sv[r]);
-            }
-          } else {
-            // bf16 P; the denominator sums the rounded P that the numerator uses
-            const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-            const int q2 = piece - 6;
-            bf16x8 bv;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pr = {static_cast<__bf16>(sv[8 * q2 + e]), static_cast<__bf16>(sv[8 * q2 + e + 1])};
-              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-              bv[e] = pr[0];
-              bv[e + 1] = pr[1];
-            }
-            ph[q2] = bv;
-            pin(bv);
-            pin(psum);
-          }
-        };
-        auto commit = [&]() {
-          l_i = fmaf(l_i, resc, psum);
-          m_i = m_new;
-          psum = 0.f;
-        };
-        auto rescale = [&]() {
-          if (need && !fresh) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
-          }
-          fresh = false;
-        };
-
-        // S^T, keys 0-31; pen of keys 0-31 read in slots 4-7 (correction steps)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ka[i] = k_op(ks, 0, i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const Op a = ka[i & 3];
-          ka[i & 3] = k_op(ks, (i + 4) >> 3, (i + 4) & 7);
-          if (KIND == 2 && i >= 4) pv[i - 4] = penp[i - 4];
-          s0 = mma<DT>(a, qf[i], s0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // S^T, keys 32-63, with the softmax of keys 0-31
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const Op a = ka[i & 3];
-          if (i < 4) ka[i & 3] = k_op(ks, 1, i + 4);
-          if (i >= 6) va[i - 6] = v_op(vt, 0, i - 6);
-          s1 = mma<DT>(a, qf[i], s1);
-          soft_piece(s0, 0, i, p0);
-          if (KIND == 2 && i == 7) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) pv[r4] = penp[4 + r4];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        commit();
-        rescale();
-        // P V, keys 0-31, with the softmax of keys 32-63
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const Op a = va[i & 1];
-          va[i & 1] = v_op(vt, (i + 2) >> 1 & 3, (i + 2 < 8) ? ((i + 2) & 1) : 2 + (i & 1));
-          oacc[i >> 1] = mma<DT>(a, p0[i & 1], oacc[i >> 1]);
-          soft_piece(s1, 1, i, p1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        commit();
-        rescale();
-        // P V, keys 32-63
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const Op a = va[i & 1];
-          if (i + 2 < 8) va[i & 1] = v_op(vt, (i + 2) >> 1, 2 + (i & 1));
-          oacc[i >> 1] = mma<DT>(a, p1[i & 1], oacc[i >> 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
       f32x16 sacc[2];
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
@@ -898,25 +1087,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 
         // P^T as the B operands of O^T += V^T P^T
         Op pf[C::NM1];
-        if constexpr (DT == kBF16) {
-          // the denominator sums the bf16-rounded P that the numerator uses
-          const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-          float psum = 0.f;
-#pragma unroll
-          for (int m1 = 0; m1 < 4; ++m1) {
-            bf16x8 b;
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const bf16x2 pr = {static_cast<__bf16>(sacc[m1 >> 1][8 * (m1 & 1) + e]),
-                                 static_cast<__bf16>(sacc[m1 >> 1][8 * (m1 & 1) + e + 1])};
-              psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-              b[e] = pr[0];
-              b[e + 1] = pr[1];
-            }
-            pf[m1] = b;
-          }
-          l_i += psum;
-        } else if constexpr (DT == kE4M3) {
+        if constexpr (DT == kE4M3) {
           float psum = 0.f;
           i32x8 b;
 #pragma unroll
@@ -993,28 +1164,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
           Op ph[C::NM1 / 2];
           float psum = 0.f;
-          if constexpr (DT == kBF16) {
-            // the denominator sums the bf16-rounded P that the numerator uses
-            const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              bf16x8 bv;
-#pragma unroll
-              for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pr = {static_cast<__bf16>(sv[8 * q2 + e]), static_cast<__bf16>(sv[8 * q2 + e + 1])};
-                psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);
-                bv[e] = pr[0];
-                bv[e + 1] = pr[1];
-              }
-              ph[q2] = bv;
-            }
-          } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               psum += sv[r];
               ph[r] = sv[r];
             }
-          }
           l_i = fmaf(l_i, resc, psum);
           m_i = m_new;
           // P is complete here, before the rescale branch, so that its VALU
@@ -1035,7 +1189,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               oacc[nt] = mma<DT>(v_op(vt, nt, jt * (C::NM1 / 2) + q2), ph[q2], oacc[nt]);
         }
       }
-      }
       if (nxt < it1) store_step(buf ^ 1, nxt);
       if constexpr (C::DMA) wait_vmem();
       __syncthreads();
@@ -1050,6 +1203,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     while (cur < it1 && cur < T) run_step(KTile{});
     if constexpr (!DENSE) {
       while (cur < it1) run_step(KChunk{});
+    }
+
     }
 
     // ---- epilogue: results as floats; a unit that saw malformed input stores
