@@ -661,10 +661,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             mh = fmaxf(ma, fmaxf(mb, sv[15]));
             pin(mh);
           } else if (k == 5) {
-            // the other lane half holds the same query row: swap halves and combine
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
-                                                             __builtin_bit_cast(uint32_t, mh), false, false);
-            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+            // the other lane half holds the same query row
+            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
             const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
             need = __any(m_half > m_i + kTau);
             m_new = need ? fmaxf(m_i, m_half) : m_i;
@@ -1149,10 +1147,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           a = fmaxf(a, fmaxf(sv[7], b));
           float mh = fmaxf(a, sv[15]);
           {
-            // the other lane half holds the same query row: swap halves and combine
-            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mh),
-                                                             __builtin_bit_cast(uint32_t, mh), false, false);
-            mh = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+            // the other lane half holds the same query row
+            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
           }
           const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
           const bool need = __any(m_half > m_i + kTau);

@@ -35,28 +35,42 @@ __device__ __forceinline__ void stage_q(const Geo& g, const SegCoord& c, const T
                                         const void* q, uint16_t* qh, uint16_t* ql) {
   const int tid = threadIdx.x;
   const int64_t r0 = c.I * kRows;
+  // all of a thread's loads are issued before the first is used
   if constexpr (DT == kBF16) {
-    for (int i = tid; i < kRows * 16; i += 256) {
-      int r = i >> 4, ch = i & 15;
-      uint4 w = make_uint4(0, 0, 0, 0);
+    uint4 w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
+      w[k] = make_uint4(0, 0, 0, 0);
       if (r < t.nrows) {
         int64_t pr = r0 + r;
         int64_t row = c.row0 + (pr >> g.log2g);
         int head = c.h * g.g + (int)(pr & (g.g - 1));
-        w = *(const uint4*)((const uint16_t*)q + (row * g.hq + head) * kD + ch * 8);
+        w[k] = *(const uint4*)((const uint16_t*)q + (row * g.hq + head) * kD + ch * 8);
       }
-      *(uint4*)(qh + r * kQPitch + ch * 8) = w;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = tid + 256 * k, r = i >> 4, ch = i & 15;
+      *(uint4*)(qh + r * kQPitch + ch * 8) = w[k];
     }
   } else if constexpr (DT == kE4M3) {
-    for (int i = tid; i < kRows * 8; i += 256) {
-      int r = i >> 3, ch = i & 7;
-      uint4 w = make_uint4(0, 0, 0, 0);
+    uint4 wv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + 256 * k, r = i >> 3, ch = i & 7;
+      wv[k] = make_uint4(0, 0, 0, 0);
       if (r < t.nrows) {
         int64_t pr = r0 + r;
         int64_t row = c.row0 + (pr >> g.log2g);
         int head = c.h * g.g + (int)(pr & (g.g - 1));
-        w = *(const uint4*)((const uint8_t*)q + (row * g.hq + head) * kD + ch * 16);
+        wv[k] = *(const uint4*)((const uint8_t*)q + (row * g.hq + head) * kD + ch * 16);
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + 256 * k, r = i >> 3, ch = i & 7;
+      const uint4 w = wv[k];
       uint32_t ww[4] = {w.x, w.y, w.z, w.w};
       uint16_t o[16];
 #pragma unroll
@@ -70,15 +84,22 @@ __device__ __forceinline__ void stage_q(const Geo& g, const SegCoord& c, const T
       dst[1] = *(uint4*)&o[8];
     }
   } else {
-    for (int i = tid; i < kRows * 32; i += 256) {
-      int r = i >> 5, ch = i & 31;
-      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 wv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = tid + 256 * k, r = i >> 5, ch = i & 31;
+      wv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (r < t.nrows) {
         int64_t pr = r0 + r;
         int64_t row = c.row0 + (pr >> g.log2g);
         int head = c.h * g.g + (int)(pr & (g.g - 1));
-        w = *(const float4*)((const float*)q + (row * g.hq + head) * kD + ch * 4);
+        wv[k] = *(const float4*)((const float*)q + (row * g.hq + head) * kD + ch * 4);
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = tid + 256 * k, r = i >> 5, ch = i & 31;
+      const float4 w = wv[k];
       float f[4] = {w.x, w.y, w.z, w.w};
       uint16_t oh[4], ol[4];
 #pragma unroll
@@ -111,8 +132,6 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  stage_q<DT>(g, c, t, q, qh, ql);
-  __syncthreads();
 
   const float sl = g.scale * 1.4426950408889634f * (DT == kE4M3 ? g.descale[0] : 1.f);
   const int nc = t.beta + 1;
@@ -122,14 +141,25 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   const int64_t jt0 = g.blk_base[c.b] >> 5;
   const int half = lane >> 5, col = lane & 31;
 
-  for (int jt = wave; jt < njt; jt += 4) {
-    const int64_t fb = (((jt0 + jt) * g.hkv + c.h) * 8) * 64 + lane;
-    bf16x8 bh[8], bl[8];
+  // the B operands (kbar hi, lo) of column tile jt: 32 blocks x 128 dims, the
+  // segment's column tiles one fragment stride apart
+  const bf16x8* khs = khi + ((jt0 * g.hkv + c.h) * 8) * 64;
+  const bf16x8* kls = klo + ((jt0 * g.hkv + c.h) * 8) * 64;
+  const int64_t jstride = (int64_t)g.hkv * 8 * 64;
+  const int nrows = t.nrows;
+  auto kb_load = [&](int jt, bf16x8 (&bh)[8], bf16x8 (&bl)[8]) {
+    const bf16x8* ph = khs + jt * jstride;
+    const bf16x8* pl = kls + jt * jstride;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      bh[ks] = khi[fb + ks * 64];
-      bl[ks] = klo[fb + ks * 64];
+      bh[ks] = ph[ks * 64 + lane];
+      bl[ks] = pl[ks * 64 + lane];
     }
+  };
+  // logits of the 128 rows x 32 blocks of column tile jt; per block (= lane
+  // column) the maximum and the sum of 2^(logit - max), logits in log2 units
+  auto tile = [&](auto ragged_tag, int jt, const bf16x8 (&bh)[8], const bf16x8 (&bl)[8]) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
     f32x16 acc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -146,30 +176,65 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
         }
       }
     }
-    // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4
-    float mx = -INFINITY;
+    // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4; padding
+    // rows of a ragged tile are masked out
+    if constexpr (RAGGED) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) acc[rt][r] = -INFINITY;
+    }
+    // raw maximum (sl > 0), then one fma per exponent
+    float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int row = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        float x = row < t.nrows ? acc[rt][r] * sl : -INFINITY;
-        acc[rt][r] = x;
-        mx = fmaxf(mx, x);
+      for (int r = 0; r < 16; r += 4) {
+        m0 = fmaxf(m0, fmaxf(acc[rt][r], acc[rt][r + 1]));
+        m1 = fmaxf(m1, fmaxf(acc[rt][r + 2], acc[rt][r + 3]));
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float sum = 0.f;
+    float mx = fmaxf(m0, m1);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(acc[rt][r] - mx);
+      for (int r = 0; r < 16; r += 2) {
+        s0 += __builtin_amdgcn_exp2f(fmaf(acc[rt][r], sl, -mx));
+        s1 += __builtin_amdgcn_exp2f(fmaf(acc[rt][r + 1], sl, -mx));
+      }
+    float sum = s0 + s1;
     sum += __shfl_xor(sum, 32, 64);
     const int J = jt * 32 + col;
     if (half == 0 && J < nc) {
       mJ[J] = mx;
       SJ[J] = sum;
     }
-  }
+  };
+  // the next column tile's operands load while this one computes (two
+  // register sets, used alternately); only a request's last tile is ragged
+  // the first column tile's operands load while Q is staged
+  bf16x8 ah[8], al[8], bh[8], bl[8];
+  if (wave < njt) kb_load(wave, ah, al);
+  stage_q<DT>(g, c, t, q, qh, ql);
+  __syncthreads();
+  auto sweep = [&](auto ragged_tag) {
+    int jt = wave;
+    while (jt < njt) {
+      if (jt + 4 < njt) kb_load(jt + 4, bh, bl);
+      tile(ragged_tag, jt, ah, al);
+      jt += 4;
+      if (jt >= njt) break;
+      if (jt + 4 < njt) kb_load(jt + 4, ah, al);
+      tile(ragged_tag, jt, bh, bl);
+      jt += 4;
+    }
+  };
+  if (nrows < kRows)
+    sweep(std::true_type{});
+  else
+    sweep(std::false_type{});
   __syncthreads();
 
   // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced.
