@@ -211,6 +211,26 @@ def cpu_baseline(batch, w, n_seg=64):
                       f"charged pro rata (pool {t_pool:.1f} s, segments {t_seg:.1f} s)"}
 
 
+def sweep(args):
+    """Speedup over the dense baseline and density against length (4 requests
+    of L tokens each, 4K..128K), one JSON line per length."""
+    for w in configs.SWEEP:
+        batch, _ = w.make()
+        case = Case(batch, None, w.alpha, w.sink_blocks, w.window_blocks)
+        m = measure(case, max(3, args.steps // 2), max(1, args.warmup))
+        d_ms = float(np.median(time_calls(case.dense, 3, 1)))
+        F = dense_flops(batch.lengths, batch.hq)
+        print(json.dumps({
+            "sweep": w.name, "L": batch.lengths[0], "num_reqs": len(batch.lengths),
+            "select_ms": m["select_ms"], "attn_ms": m["attn_ms"], "step_ms": m["step_ms"],
+            "dense_ms": d_ms, "speedup_vs_dense": d_ms / m["step_ms"],
+            "select_share": m["select_ms"] / m["step_ms"], "density": m["density"],
+            "eff_tflops": F / (m["step_ms"] / 1e3) / 1e12,
+            "attn_alg_tflops": m["attn_alg_flop"] / (m["attn_ms"] / 1e3) / 1e12}), flush=True)
+        del case, batch
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +242,9 @@ def main():
     ap.add_argument("--cpu-segments", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="length sweep 4K..128K at 4 requests: one JSON line per length (select, attention, "
+                         "dense baseline, speedup, density)")
     args = ap.parse_args()
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -234,6 +257,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
 
     w = configs.ALL[args.config]
     t0 = time.time()

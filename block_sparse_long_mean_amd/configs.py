@@ -48,4 +48,9 @@ VARLEN = Workload("paged_varlen_16req_bf16",
                   tuple(synth.varlen_lengths(16, 4096, 131072, 4)), 32, 4, 128, "bf16", 4, 0.1, 2,
                   4, True, True, page_size=64)
 
-ALL = {w.name: w for w in (TINY, L32K, L128K, L128K_FP8, VARLEN)}
+# Length sweep: 4 requests of equal length L, 4K..128K, same generator and
+# selection settings as the 128K layer (one seed per length).
+SWEEP = tuple(Workload(f"sweep_{L // 1024}k_x4_bf16", (L,) * 4, 32, 4, 128, "bf16", 100 + i, 0.1, 2, 4, True,
+                       True) for i, L in enumerate((4096, 8192, 16384, 32768, 65536, 131072)))
+
+ALL = {w.name: w for w in (TINY, L32K, L128K, L128K_FP8, VARLEN) + SWEEP}

@@ -6,6 +6,8 @@
   ragged last tile included; pooled means for every block.
 - Paged varlen (16 requests, 64-token pages, NaN-poisoned pool): 4 segments
   per request.
+- Length sweep, 4 requests of 4K (full CSR, 256 sampled segments) and of 16K
+  (64 sampled segments), correction on and off.
 The oracle computes each sampled segment on its own (pooling of all blocks,
 scoring, selection, corrected attention on the GPU's own index).
 """
@@ -140,3 +142,23 @@ def test_paged_varlen_sampled():
         got = sum(int(cu[s + 1] - cu[s]) for s in range(s0, s1, 97))
         dens.append(got / max(1, cand))
     _note("  per-request density (every 97th segment): " + " ".join(f"{d:.3f}" for d in dens))
+
+
+@pytest.mark.parametrize("name,n_attn,full_csr", [("sweep_4k_x4_bf16", 256, True),
+                                                  ("sweep_16k_x4_bf16", 64, False)])
+def test_length_sweep_sampled(name, n_attn, full_csr):
+    """Length-sweep workloads (4 requests of equal length): the short end of the
+    sweep, where every request has few blocks and the forced set dominates."""
+    w = configs.ALL[name]
+    _note(f"[case] {w.name}")
+    b, _ = w.make()
+    run = GpuRun(b, alpha=w.alpha, sink=w.sink_blocks, win=w.window_blocks)
+    cu, idx = run.select()
+    P = oracle_for(run)
+    _check_pool(run, P)
+    segs = sample_segments(P, n_attn, seed=7)
+    n, amb = compare_csr(P, cu, idx, w.alpha, w.sink_blocks, w.window_blocks, segs=None if full_csr else segs)
+    _note(f"  CSR: {n} segments, {amb} band differences")
+    _attn_check(run, P, segs, cu, idx, "bf16", correction=True)
+    _attn_check(run, P, segs, cu, idx, "bf16", correction=False)
+    assert run.device_error() == 0
