@@ -15,6 +15,9 @@ Recipe, per request b and KV head h (numpy PCG64 seeded by (seed, b, h)):
 and for the j-th query head of the group (seeded by (seed, b, h, 1+j)):
   q_t = N(0, I_d) + 1.5u;  with ``diag_bias``, r ~ U{1..64} and
   q_t += 0.5 k_{t-r} for t >= r.
+A request with L_q < L queries (a prefill chunk after a cached prefix) keeps
+the last L_q rows of the same q_t draws, so its queries are exactly those of
+the fresh request at positions L-L_q..L-1.
 Everything is drawn in float32, then cast with round-to-nearest-even.  E4M3
 inputs are quantised from the bf16 tensors with per-tensor scales
 c = amax|X| / 448 (OCP E4M3FN, saturated at +-448).
@@ -43,7 +46,9 @@ def _rng(*key):
 
 @dataclass
 class Batch:
-    """One batch of requests, contiguous layout ([total, H, d], ragged by cu)."""
+    """One batch of requests, contiguous layout: Q [total_q, Hq, d] ragged by
+    ``cu``, K/V [total_kv, Hkv, d] ragged by ``cu_kv`` (None: by ``cu``).
+    ``lengths`` are the K/V lengths, ``q_lengths`` the query lengths."""
 
     lengths: list
     hq: int
@@ -55,14 +60,33 @@ class Batch:
     v: torch.Tensor
     descale: tuple = (1.0, 1.0, 1.0)
     cu: np.ndarray = field(default=None)
+    q_lengths: list = field(default=None)
+    cu_kv: np.ndarray = field(default=None)
 
     def __post_init__(self):
+        if self.q_lengths is None:
+            self.q_lengths = list(self.lengths)
         if self.cu is None:
-            self.cu = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int64)
+            self.cu = np.concatenate([[0], np.cumsum(self.q_lengths)]).astype(np.int64)
+        if self.cu_kv is None and list(self.q_lengths) != list(self.lengths):
+            self.cu_kv = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int64)
+
+    @property
+    def chunked(self) -> bool:
+        return self.cu_kv is not None
+
+    @property
+    def kv_cu(self) -> np.ndarray:
+        return self.cu if self.cu_kv is None else self.cu_kv
 
     @property
     def total(self) -> int:
+        """Query rows."""
         return int(self.cu[-1])
+
+    @property
+    def total_kv(self) -> int:
+        return int(self.kv_cu[-1])
 
     def storage(self, t: torch.Tensor) -> np.ndarray:
         """Raw host view for the oracle: float32, uint16 (bf16 bits) or uint8."""
@@ -71,7 +95,7 @@ class Batch:
         return t.numpy()
 
 
-def _gen_head(seed, b, h, L, d, g, clusters, diag_bias, q_out, k_out, v_out, q_dtype, kv_dtype):
+def _gen_head(seed, b, h, L, Lq, d, g, clusters, diag_bias, q_out, k_out, v_out, q_dtype, kv_dtype):
     rng = _rng(seed, b, h)
     nJ = (L + BLOCK - 1) // BLOCK
     m = rng.standard_normal((nJ, d), dtype=np.float32)
@@ -95,30 +119,37 @@ def _gen_head(seed, b, h, L, d, g, clusters, diag_bias, q_out, k_out, v_out, q_d
         q += 1.5 * u
         if diag_bias and r < L:
             q[r:] += 0.5 * k[: L - r]
-        q_out[:, h * g + j, :] = torch.from_numpy(q).to(q_dtype)
+        q_out[:, h * g + j, :] = torch.from_numpy(q[L - Lq:]).to(q_dtype)
 
 
-def make_batch(lengths, hq, hkv, d, seed, dtype="bf16", clusters=False, diag_bias=False) -> Batch:
-    """Draw a batch; ``dtype`` "f32" or "bf16" (use :func:`to_e4m3` for E4M3)."""
+def make_batch(lengths, hq, hkv, d, seed, dtype="bf16", clusters=False, diag_bias=False,
+               q_lengths=None) -> Batch:
+    """Draw a batch; ``dtype`` "f32" or "bf16" (use :func:`to_e4m3` for E4M3).
+    ``lengths`` are the K/V lengths; ``q_lengths`` (None: the same) the number of
+    trailing positions of each request that carry queries."""
     lengths = [int(x) for x in lengths]
+    qls = list(lengths) if q_lengths is None else [int(x) for x in q_lengths]
+    assert len(qls) == len(lengths) and all(0 <= a <= L for a, L in zip(qls, lengths))
     g = hq // hkv
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
-    total = sum(lengths)
-    q = torch.empty((total, hq, d), dtype=tdt)
-    k = torch.empty((total, hkv, d), dtype=tdt)
-    v = torch.empty((total, hkv, d), dtype=tdt)
+    q = torch.empty((sum(qls), hq, d), dtype=tdt)
+    k = torch.empty((sum(lengths), hkv, d), dtype=tdt)
+    v = torch.empty((sum(lengths), hkv, d), dtype=tdt)
     jobs = []
-    off = 0
-    for b, L in enumerate(lengths):
+    off = qoff = 0
+    for b, (L, Lq) in enumerate(zip(lengths, qls)):
         for h in range(hkv):
-            jobs.append((b, h, L, off))
+            jobs.append((b, h, L, Lq, off, qoff))
         off += L
+        qoff += Lq
     with ThreadPoolExecutor(_workers()) as ex:
-        futs = [ex.submit(_gen_head, seed, b, h, L, d, g, clusters, diag_bias,
-                          q[o:o + L], k[o:o + L], v[o:o + L], tdt, tdt) for (b, h, L, o) in jobs]
+        futs = [ex.submit(_gen_head, seed, b, h, L, Lq, d, g, clusters, diag_bias,
+                          q[qo:qo + Lq], k[o:o + L], v[o:o + L], tdt, tdt)
+                for (b, h, L, Lq, o, qo) in jobs]
         for f in futs:
             f.result()
-    return Batch(lengths, hq, hkv, d, dtype, q, k, v)
+    return Batch(lengths, hq, hkv, d, dtype, q, k, v,
+                 q_lengths=None if q_lengths is None else qls)
 
 
 def _quant_e4m3(x: torch.Tensor):
@@ -143,7 +174,15 @@ def to_e4m3(batch: Batch) -> Batch:
     kc, ck = _quant_e4m3(batch.k)
     vc, cv = _quant_e4m3(batch.v)
     return Batch(batch.lengths, batch.hq, batch.hkv, batch.d, "e4m3", qc, kc, vc,
-                 descale=(cq, ck, cv), cu=batch.cu)
+                 descale=(cq, ck, cv), cu=batch.cu, q_lengths=batch.q_lengths, cu_kv=batch.cu_kv)
+
+
+def prefix_chunk(batch: Batch, stop: int, size: int) -> Batch:
+    """Chunk [stop - size, stop) of a one-request batch's prompt: its queries and
+    every key/value before ``stop`` (views, no copy)."""
+    assert len(batch.lengths) == 1 and not batch.chunked and 0 < size <= stop <= batch.lengths[0]
+    return Batch([stop], batch.hq, batch.hkv, batch.d, batch.dtype, batch.q[stop - size:stop],
+                 batch.k[:stop], batch.v[:stop], descale=batch.descale, q_lengths=[size])
 
 
 def varlen_lengths(n, lo, hi, seed):
@@ -192,7 +231,7 @@ def page_kv(batch: Batch, page_size, seed, spare=0.05, poison=True) -> Paged:
             kp.fill_(float("nan"))
             vp.fill_(float("nan"))
     for b, L in enumerate(batch.lengths):
-        base = int(batch.cu[b])
+        base = int(batch.kv_cu[b])
         for j in range(need[b]):
             lo = j * page_size
             hi = min(L, lo + page_size)

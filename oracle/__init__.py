@@ -44,6 +44,7 @@ class _Prob(C.Structure):
         ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
         ("scale", C.c_double),
         ("block", C.c_int32), ("rows", C.c_int32), ("phys", C.c_int32),
+        ("cu_kv", C.POINTER(C.c_int64)),
     ]
 
 
@@ -81,7 +82,7 @@ def lib():
         L.fpo_score_tile.restype = C.c_int64
         L.fpo_score_tile.argtypes = [P, dp, C.c_int, C.c_int, C.c_int64, C.c_int, dp]
         L.fpo_select_tile.restype = None
-        L.fpo_select_tile.argtypes = [dp, C.c_int64, C.c_double, C.c_int, C.c_int, u8p, u8p]
+        L.fpo_select_tile.argtypes = [dp, C.c_int64, C.c_int64, C.c_double, C.c_int, C.c_int, u8p, u8p]
         L.fpo_csr_tile.restype = C.c_int64
         L.fpo_csr_tile.argtypes = [u8p, C.c_int64, C.c_int64, C.c_int, C.c_int, i32p]
         L.fpo_select_all.restype = C.c_int64
@@ -119,12 +120,14 @@ def num_threads() -> int:
 class Problem:
     """Host description of one batch for the oracle.
 
-    ``q`` is [total, hq, d], ``k``/``v`` are [total, hkv, d] (contiguous rows,
-    ragged by ``cu``), stored as described in the module docstring.
+    ``q`` is [total_q, hq, d] ragged by ``cu``; ``k``/``v`` are [total_kv, hkv, d]
+    ragged by ``cu_kv`` (None: by ``cu``), contiguous, stored as described in
+    the module docstring.  A request with more keys than queries holds a prefill
+    chunk: its queries are its last L_q positions.
     """
 
     def __init__(self, cu, hq, hkv, d, dtype, q, k, v, descale=(1.0, 1.0, 1.0), scale=None,
-                 block=128, rows=128, phys=64, _geometry_only=False):
+                 block=128, rows=128, phys=64, cu_kv=None, _geometry_only=False):
         if dtype not in DTYPES:
             raise ValueError(dtype)
         st = _NP_STORAGE[dtype]
@@ -132,10 +135,14 @@ class Problem:
         self.k = np.ascontiguousarray(k).view(st) if k.dtype != st else np.ascontiguousarray(k)
         self.v = np.ascontiguousarray(v).view(st) if v.dtype != st else np.ascontiguousarray(v)
         self.cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int64))
-        total = int(self.cu[-1])
+        self.cu_kv = None if cu_kv is None else np.ascontiguousarray(np.asarray(cu_kv, dtype=np.int64))
+        kvc = self.cu if self.cu_kv is None else self.cu_kv
+        assert len(kvc) == len(self.cu) and kvc[0] == 0
+        assert np.all(np.diff(kvc) >= np.diff(self.cu)), "every request needs L_kv >= L_q"
+        total, total_kv = int(self.cu[-1]), int(kvc[-1])
         if not _geometry_only:
             assert self.q.shape == (total, hq, d), (self.q.shape, total, hq, d)
-            assert self.k.shape == (total, hkv, d) and self.v.shape == (total, hkv, d)
+            assert self.k.shape == (total_kv, hkv, d) and self.v.shape == (total_kv, hkv, d)
         self.hq, self.hkv, self.d, self.dtype = hq, hkv, d, dtype
         self.block, self.rows, self.phys = block, rows, phys
         self.scale = float(scale) if scale is not None else 1.0 / float(np.sqrt(d))
@@ -145,17 +152,20 @@ class Problem:
             self.descale[0], self.descale[1], self.descale[2],
             self.q.ctypes.data, self.k.ctypes.data, self.v.ctypes.data,
             self.scale, block, rows, phys,
+            None if self.cu_kv is None else _ptr(self.cu_kv, C.c_int64),
         )
         self._kbar = None
         self._vbar = None
 
     @classmethod
-    def geometry(cls, lengths, hq, hkv, d=128, block=128, rows=128, phys=64):
-        """A problem usable only for its geometry (segments, tiles, blocks)."""
-        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    def geometry(cls, lengths, hq, hkv, d=128, block=128, rows=128, phys=64, q_lengths=None):
+        """A problem usable only for its geometry (segments, tiles, blocks).
+        ``lengths`` are the K/V lengths, ``q_lengths`` the query lengths (None: the same)."""
+        cu_kv = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+        cu = cu_kv if q_lengths is None else np.concatenate([[0], np.cumsum(q_lengths)]).astype(np.int64)
         z = np.zeros((1, 1, 1), np.float32)
         return cls(cu, hq, hkv, d, "f32", z, z, z, block=block, rows=rows, phys=phys,
-                   _geometry_only=True)
+                   cu_kv=None if q_lengths is None else cu_kv, _geometry_only=True)
 
     # -- geometry -------------------------------------------------------
     @property
@@ -199,20 +209,26 @@ class Problem:
         return self._kbar, self._vbar
 
     # -- scoring / selection -------------------------------------------
+    def candidates(self, b, I) -> int:
+        """Candidate blocks of tile I: every block up to that of its last position."""
+        _, _, t1, _ = self.tile_info(b, I)
+        return t1 // self.block + 1
+
     def score_tile(self, b, h, I, form=2):
         kb, _ = self.pool()
-        _, _, _, beta = self.tile_info(b, I)
-        e = np.zeros(beta + 1, np.float64)
+        e = np.zeros(self.candidates(b, I), np.float64)
         lib().fpo_score_tile(C.byref(self._s), _ptr(kb, C.c_double), b, h, I, form,
                              _ptr(e, C.c_double))
         return e
 
     @staticmethod
-    def select_tile(e, alpha, n_sink, n_win):
+    def select_tile(e, alpha, n_sink, n_win, beta=None):
+        """``beta``: the block of the tile's first position (None: the last candidate)."""
         e = np.ascontiguousarray(e, np.float64)
         sel = np.zeros(len(e), np.uint8)
         amb = np.zeros(len(e), np.uint8)
-        lib().fpo_select_tile(_ptr(e, C.c_double), len(e), alpha, n_sink, n_win,
+        beta = len(e) - 1 if beta is None else beta
+        lib().fpo_select_tile(_ptr(e, C.c_double), len(e), beta, alpha, n_sink, n_win,
                               _ptr(sel, C.c_uint8), _ptr(amb, C.c_uint8))
         return sel.astype(bool), amb.astype(bool)
 
@@ -227,9 +243,9 @@ class Problem:
     def segment_select(self, s, alpha, n_sink, n_win, form=2):
         """(e, sel, ambig, idx) of one segment."""
         b, h, I = self.segment_coords(s)
-        _, _, t1, _ = self.tile_info(b, I)
+        _, _, t1, beta = self.tile_info(b, I)
         e = self.score_tile(b, h, I, form)
-        sel, amb = self.select_tile(e, alpha, n_sink, n_win)
+        sel, amb = self.select_tile(e, alpha, n_sink, n_win, beta)
         return e, sel, amb, self.csr_tile(sel, t1)
 
     def max_candidates(self) -> int:
@@ -242,8 +258,7 @@ class Problem:
         cap = 0
         for s in range(nseg):
             b, h, I = self.segment_coords(s)
-            _, _, _, beta = self.tile_info(b, I)
-            cap += (beta + 1) * (self.block // self.phys)
+            cap += self.candidates(b, I) * (self.block // self.phys)
         cu = np.zeros(nseg + 1, np.int32)
         idx = np.zeros(max(cap, 1), np.int32)
         mx = self.max_candidates()
@@ -300,11 +315,11 @@ class Problem:
 
     # -- row mapping (definition of PackGQA, [V2] §3.3 Eq. 13) -----------
     def rows_of_segment(self, s):
-        """(positions, heads, valid) of the R packed rows of segment s."""
+        """(Q rows, heads, valid) of the R packed rows of segment s."""
         b, h, I = self.segment_coords(s)
         r = I * self.rows + np.arange(self.rows)
-        L = int(self.cu[b + 1] - self.cu[b])
-        valid = r < self.g * L
-        pos = r // self.g
+        Lq = int(self.cu[b + 1] - self.cu[b])
+        valid = r < self.g * Lq
+        qi = r // self.g
         head = h * self.g + r % self.g
-        return self.cu[b] + pos, head, valid
+        return self.cu[b] + qi, head, valid

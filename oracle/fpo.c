@@ -20,10 +20,15 @@
  *
  * Conventions shared with every caller (they are definitions of the problem,
  * not of the GPU path):
- *   - q is [total, hq, d], k and v are [total, hkv, d], ragged by cu[] rows
- *     (contiguous; paged inputs are de-paged by the caller with [V2] Eq. 22).
- *   - packed row r of KV head h maps to position floor(r/g) and query head
- *     h*g + (r mod g)                                     ([V2] §3.3 Eq. 12-13)
+ *   - q is [total_q, hq, d] ragged by cu[]; k and v are [total_kv, hkv, d]
+ *     ragged by cu_kv[] (NULL: by cu[]) (contiguous; paged inputs are de-paged
+ *     by the caller with [V2] Eq. 22).
+ *   - a request has L_kv keys and L_q <= L_kv queries, which are its last L_q
+ *     positions: query i sits at position off + i, off = L_kv - L_q (a prefill
+ *     chunk after a cached prefix, the index re-run for every chunk: [V2] §4.3
+ *     "Compatibility with Chunked Prefill"; off = 0 for a fresh prefill).
+ *   - packed row r of KV head h is query floor(r/g), at position
+ *     off + floor(r/g), of query head h*g + (r mod g)     ([V2] §3.3 Eq. 12-13)
  *   - a query tile is R consecutive packed rows of one (request, KV head);
  *     segments are ordered (request, KV head, tile).      ([V2] §3.3 Eq. 17)
  *   - blocks are B tokens, physical tiles are P tokens.   ([V2] §3.3 impl. details)
@@ -51,6 +56,7 @@ typedef struct {
   int32_t block;      /* B, selection block size */
   int32_t rows;       /* R, packed rows per query tile */
   int32_t phys;       /* P, physical key tile */
+  const int64_t* cu_kv; /* [num_reqs+1] row offsets into k/v, or NULL: the same as cu */
 } fpo_problem;
 
 /* ------------------------------------------------------------------ */
@@ -132,7 +138,15 @@ static double dot(const double* a, const double* b, int n) {
 /* geometry                                                             */
 /* ------------------------------------------------------------------ */
 
-static int64_t req_len(const fpo_problem* p, int b) { return p->cu[b + 1] - p->cu[b]; }
+/* key/value length L_kv, query length L_q, first query position and first
+ * K/V row of request b */
+static int64_t req_len(const fpo_problem* p, int b) {
+  const int64_t* c = p->cu_kv ? p->cu_kv : p->cu;
+  return c[b + 1] - c[b];
+}
+static int64_t q_len(const fpo_problem* p, int b) { return p->cu[b + 1] - p->cu[b]; }
+static int64_t q_off(const fpo_problem* p, int b) { return req_len(p, b) - q_len(p, b); }
+static int64_t kv_start(const fpo_problem* p, int b) { return p->cu_kv ? p->cu_kv[b] : p->cu[b]; }
 static int group(const fpo_problem* p) { return p->hq / p->hkv; }
 
 int64_t fpo_blocks_in_req(const fpo_problem* p, int b) {
@@ -147,7 +161,7 @@ int64_t fpo_block_offset(const fpo_problem* p, int b) {
 }
 
 int64_t fpo_tiles_in_req(const fpo_problem* p, int b) {
-  int64_t packed = (int64_t)group(p) * req_len(p, b);
+  int64_t packed = (int64_t)group(p) * q_len(p, b);
   return (packed + p->rows - 1) / p->rows;
 }
 
@@ -176,18 +190,18 @@ void fpo_segment_coords(const fpo_problem* p, int64_t s, int32_t* b_out, int32_t
   *i_out = -1;
 }
 
-/* Tile I of (b, h): packed rows [I*R, min((I+1)R, g*L)), first/last position
- * t0/t1 and its block beta = floor(t0/B) ([V2] §3.3 Eq. 13).  Returns the
- * number of valid rows. */
+/* Tile I of (b, h): packed rows [I*R, min((I+1)R, g*L_q)), first/last position
+ * t0/t1 (off included) and its block beta = floor(t0/B) ([V2] §3.3 Eq. 13).
+ * Returns the number of valid rows. */
 int fpo_tile_info(const fpo_problem* p, int b, int64_t I, int64_t* t0, int64_t* t1,
                   int64_t* beta) {
   int g = group(p);
-  int64_t packed = (int64_t)g * req_len(p, b);
+  int64_t packed = (int64_t)g * q_len(p, b);
   int64_t r0 = I * p->rows;
   int64_t r1 = r0 + p->rows;
   if (r1 > packed) r1 = packed;
-  *t0 = r0 / g;
-  *t1 = (r1 - 1) / g;
+  *t0 = q_off(p, b) + r0 / g;
+  *t1 = q_off(p, b) + (r1 - 1) / g;
   *beta = *t0 / p->block;
   return (int)(r1 - r0);
 }
@@ -216,9 +230,9 @@ void fpo_pool_all(const fpo_problem* p, double* kbar, double* vbar) {
       double* vo = vbar + ((size_t)gb * p->hkv + h) * p->d;
       for (int i = 0; i < p->d; ++i) ko[i] = vo[i] = 0.0;
       for (int64_t t = lo; t < hi; ++t) {
-        load_k(p, p->cu[b] + t, h, kv);
+        load_k(p, kv_start(p, b) + t, h, kv);
         for (int i = 0; i < p->d; ++i) ko[i] += kv[i];
-        load_v(p, p->cu[b] + t, h, kv);
+        load_v(p, kv_start(p, b) + t, h, kv);
         for (int i = 0; i < p->d; ++i) vo[i] += kv[i];
       }
       for (int i = 0; i < p->d; ++i) {
@@ -240,9 +254,14 @@ static const double* kbar_row(const fpo_problem* p, const double* kbar, int64_t 
 /* block energies of one tile ([V2] §3.1 Eq. 1-3, §3.3 Eq. 19-20)        */
 /* ------------------------------------------------------------------ */
 
-/* Candidate blocks are J in [0, beta], the diagonal block included and scored
- * with its full pooled mean (READING: the causal constraint of [V2] Eq. 3 and
- * thresh = alpha * max_{J <= I} of [V1] §3.4).  The logit carries the softmax
+/* Candidate blocks are J in [0, beta1], beta1 = floor(t1/B) the block of the
+ * tile's last position, the diagonal blocks included and scored with their full
+ * pooled means (READING: the causal constraint of [V2] Eq. 3 and
+ * thresh = alpha * max_{J <= I} of [V1] §3.4).  A fresh prefill's tile lies in
+ * one block (beta1 = beta); a chunk whose first position is not a multiple of
+ * R/g can put a tile across blocks beta and beta + 1 (READING, chunked prefill
+ * of [V2] §4.3: every block holding a key visible to some row of the tile is a
+ * candidate).  The logit carries the softmax
  * scale sigma as in [V2] Eq. 5 and Eq. 19 (READING: [V2] Eq. 1 omits it).
  *
  * form 0 -- direct: s_rJ = sigma q_r.k_bar_J, M = max_{r,J} s_rJ,
@@ -256,19 +275,19 @@ static const double* kbar_row(const fpo_problem* p, const double* kbar, int64_t 
  *           chunk's M stored as M_c; finally E_J <- E_J 2^(M_c - M_final).
  *
  * All forms return e_J = E_J / max_J' E_J' in (0, 1] (the normalised energy
- * that [V2] Eq. 3 / Eq. 20 compare against alpha).  Returns beta + 1. */
+ * that [V2] Eq. 3 / Eq. 20 compare against alpha).  Returns beta1 + 1. */
 int64_t fpo_score_tile(const fpo_problem* p, const double* kbar, int b, int h, int64_t I,
                        int form, double* e_out) {
   int g = group(p);
   int64_t t0, t1, beta;
   int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
-  int64_t nc = beta + 1;
+  int64_t nc = t1 / p->block + 1;
   int d = p->d;
   double* qv = (double*)malloc(sizeof(double) * (size_t)nrows * d);
   double* s = (double*)malloc(sizeof(double) * (size_t)nrows * nc);
   for (int r = 0; r < nrows; ++r) {
     int64_t pr = I * p->rows + r;
-    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv + (size_t)r * d);
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv + (size_t)r * d); /* query pr/g */
   }
   int64_t blk0 = fpo_block_offset(p, b);
   for (int r = 0; r < nrows; ++r)
@@ -336,15 +355,15 @@ int64_t fpo_score_tile(const fpo_problem* p, const double* kbar, int b, int h, i
 /* ------------------------------------------------------------------ */
 
 /* Keep J iff e_J >= alpha (inclusive), or J is a sink block (J < n_sink), a
- * window block (the n_win blocks just before beta), or the diagonal block
- * beta ([V2] §3.1 "Max-based Dynamic Thresholding"; defaults in §4.1).
+ * window block (the n_win blocks just before beta), or a diagonal block
+ * J >= beta, i.e. one holding a position of the tile ([V2] §3.1 "Max-based
+ * Dynamic Thresholding"; defaults in §4.1).  The candidates are J < nc.
  * ambig[J] marks unforced blocks with |e_J - alpha| <= 1e-4 alpha, where two
  * correct implementations may legitimately disagree. */
-void fpo_select_tile(const double* e, int64_t nc, double alpha, int n_sink, int n_win,
-                     uint8_t* sel, uint8_t* ambig) {
-  int64_t beta = nc - 1;
+void fpo_select_tile(const double* e, int64_t nc, int64_t beta, double alpha, int n_sink,
+                     int n_win, uint8_t* sel, uint8_t* ambig) {
   for (int64_t J = 0; J < nc; ++J) {
-    int forced = (J < n_sink) || (J >= beta - n_win && J < beta) || (J == beta);
+    int forced = (J < n_sink) || (J >= beta - n_win && J < beta) || (J >= beta);
     sel[J] = (uint8_t)(forced || e[J] >= alpha);
     if (ambig) ambig[J] = (uint8_t)(!forced && fabs(e[J] - alpha) <= 1e-4 * alpha);
   }
@@ -374,8 +393,8 @@ int64_t fpo_csr_tile(const uint8_t* sel, int64_t nc, int64_t t1, int phys, int b
 }
 
 /* Whole-problem index: cu[n_seg+1] (exclusive prefix sum in segment order)
- * and idx.  e_out / ambig_out (optional) are [n_seg][max_nc] with max_nc the
- * largest beta+1, padded with -1 / 0.  Returns the number of idx entries, or
+ * and idx.  e_out / ambig_out (optional) are [n_seg][max_nc] with max_nc at
+ * least the largest beta1+1, padded with -1 / 0.  Returns the number of idx entries, or
  * -1 if cap is too small. */
 int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, int n_sink,
                        int n_win, int form, int32_t* cu, int32_t* idx, int64_t cap,
@@ -388,12 +407,12 @@ int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, i
     int64_t I, t0, t1, beta;
     fpo_segment_coords(p, s, &b, &h, &I);
     fpo_tile_info(p, b, I, &t0, &t1, &beta);
-    int64_t nc = beta + 1;
+    int64_t nc = t1 / p->block + 1;
     double* e = (double*)malloc(sizeof(double) * nc);
     uint8_t* sel = (uint8_t*)malloc(nc);
     uint8_t* amb = (uint8_t*)malloc(nc);
     fpo_score_tile(p, kbar, b, h, I, form, e);
-    fpo_select_tile(e, nc, alpha, n_sink, n_win, sel, amb);
+    fpo_select_tile(e, nc, beta, alpha, n_sink, n_win, sel, amb);
     counts[s] = fpo_csr_tile(sel, nc, t1, p->phys, p->block, NULL);
     if (e_out)
       for (int64_t J = 0; J < max_nc; ++J) e_out[s * max_nc + J] = J < nc ? e[J] : -1.0;
@@ -421,11 +440,11 @@ int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, i
     int64_t I, t0, t1, beta;
     fpo_segment_coords(p, s, &b, &h, &I);
     fpo_tile_info(p, b, I, &t0, &t1, &beta);
-    int64_t nc = beta + 1;
+    int64_t nc = t1 / p->block + 1;
     double* e = (double*)malloc(sizeof(double) * nc);
     uint8_t* sel = (uint8_t*)malloc(nc);
     fpo_score_tile(p, kbar, b, h, I, form, e);
-    fpo_select_tile(e, nc, alpha, n_sink, n_win, sel, NULL);
+    fpo_select_tile(e, nc, beta, alpha, n_sink, n_win, sel, NULL);
     fpo_csr_tile(sel, nc, t1, p->phys, p->block, idx + counts[s]);
     free(e);
     free(sel);
@@ -476,14 +495,14 @@ void fpo_attend_tile(const fpo_problem* p, const double* kbar, const double* vba
       continue;
     }
     int64_t pr = I * p->rows + r;
-    int64_t t = pr / g;
-    load_q(p, p->cu[b] + t, h * g + (int)(pr % g), qv);
+    int64_t t = q_off(p, b) + pr / g; /* position of the row's query */
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv);
     /* pass 1: the row maximum over every logit that enters the softmax */
     double m = -INFINITY;
     for (int64_t e = 0; e < T; ++e)
       for (int64_t i = (int64_t)idx[e] * p->phys; i < ((int64_t)idx[e] + 1) * p->phys; ++i) {
         if (i > t || i >= L) continue;
-        load_k(p, p->cu[b] + i, h, kv);
+        load_k(p, kv_start(p, b) + i, h, kv);
         double a = p->scale * dot(qv, kv, d);
         if (a > m) m = a;
       }
@@ -499,8 +518,8 @@ void fpo_attend_tile(const fpo_problem* p, const double* kbar, const double* vba
     for (int64_t e = 0; e < T; ++e)
       for (int64_t i = (int64_t)idx[e] * p->phys; i < ((int64_t)idx[e] + 1) * p->phys; ++i) {
         if (i > t || i >= L) continue;
-        load_k(p, p->cu[b] + i, h, kv);
-        load_v(p, p->cu[b] + i, h, vv);
+        load_k(p, kv_start(p, b) + i, h, kv);
+        load_v(p, kv_start(p, b) + i, h, vv);
         double w = exp(p->scale * dot(qv, kv, d) - m);
         if (p8) w = fpo_e4m3_round(256.0 * w);
         den += w;
@@ -543,19 +562,19 @@ void fpo_dense_tile(const fpo_problem* p, int b, int h, int64_t I, double* out, 
       continue;
     }
     int64_t pr = I * p->rows + r;
-    int64_t t = pr / g;
-    load_q(p, p->cu[b] + t, h * g + (int)(pr % g), qv);
+    int64_t t = q_off(p, b) + pr / g; /* position of the row's query */
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv);
     double m = -INFINITY;
     for (int64_t i = 0; i <= t; ++i) {
-      load_k(p, p->cu[b] + i, h, kv);
+      load_k(p, kv_start(p, b) + i, h, kv);
       double a = p->scale * dot(qv, kv, d);
       if (a > m) m = a;
     }
     double den = 0.0;
     for (int i = 0; i < d; ++i) num[i] = 0.0;
     for (int64_t i = 0; i <= t; ++i) {
-      load_k(p, p->cu[b] + i, h, kv);
-      load_v(p, p->cu[b] + i, h, vv);
+      load_k(p, kv_start(p, b) + i, h, kv);
+      load_v(p, kv_start(p, b) + i, h, vv);
       double w = exp(p->scale * dot(qv, kv, d) - m);
       den += w;
       for (int j = 0; j < d; ++j) num[j] += w * vv[j];

@@ -27,12 +27,14 @@ class GpuRun:
         if paged is None:
             self.k = batch.k.to(device)
             self.v = batch.v.to(device)
-            self.B = F.make_batch(batch.cu, batch.hq, batch.hkv, dt, descale=batch.descale if batch.dtype == "e4m3" else None)
+            self.B = F.make_batch(batch.cu, batch.hq, batch.hkv, dt, cu_seqlens_kv=batch.cu_kv,
+                                  descale=batch.descale if batch.dtype == "e4m3" else None)
         else:
             self.k = paged.k_pool.to(device)
             self.v = paged.v_pool.to(device)
             self.B = F.make_batch(batch.cu, batch.hq, batch.hkv, dt, page_table=paged.page_table,
                                   page_size=paged.page_size, num_pool_slots=paged.num_slots,
+                                  cu_seqlens_kv=batch.cu_kv,
                                   descale=batch.descale if batch.dtype == "e4m3" else None)
         self.params = F.select_params(alpha, sink, win)
         self.bufs = F.Buffers(self.B, self.params)
@@ -84,7 +86,7 @@ def compare_csr(P: "oracle.Problem", cu, idx, alpha, sink, win, segs=None):
         e, sel, amb, want = P.segment_select(s, alpha, sink, win)
         got = idx[cu[s]:cu[s + 1]]
         assert np.all(np.diff(got) > 0), f"segment {s}: idx not ascending"
-        blocks = np.zeros(beta + 1, bool)
+        blocks = np.zeros(P.candidates(b, I), bool)
         blocks[np.unique(got // 2)] = True
         # the list must be exactly the expansion of its blocks
         exp = P.csr_tile(blocks.astype(np.uint8), t1)

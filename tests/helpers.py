@@ -10,7 +10,7 @@ import oracle
 def oracle_problem(batch, **kw) -> "oracle.Problem":
     return oracle.Problem(batch.cu, batch.hq, batch.hkv, batch.d, batch.dtype,
                           batch.storage(batch.q), batch.storage(batch.k), batch.storage(batch.v),
-                          descale=batch.descale, **kw)
+                          descale=batch.descale, cu_kv=batch.cu_kv, **kw)
 
 
 def f32_problem(lengths, hq, hkv, d, q, k, v, **kw) -> "oracle.Problem":
