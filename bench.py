@@ -33,43 +33,52 @@ PEAK = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}  # dense MFMA TFLOP/s, MI3
 D = 128
 
 
-def dense_flops(lengths, hq):
-    return float(sum(2.0 * D * hq * L * (L + 1) for L in lengths))
+def dense_flops(lengths, hq, q_lengths=None):
+    """Causal attention FLOPs (QK^T and PV, 2 flops per multiply-add) of queries at
+    positions L - L_q .. L - 1 over keys 0 .. t."""
+    q_lengths = lengths if q_lengths is None else q_lengths
+    tot = 0.0
+    for L, Lq in zip(lengths, q_lengths):
+        off = L - Lq
+        tot += 2.0 * D * hq * (L * (L + 1) - off * (off + 1))
+    return tot
 
 
 def algorithmic_bytes(batch):
     """Least HBM bytes one attention launch must move: Q and O once, K and V once."""
     eb = {"bf16": 2, "e4m3": 1, "f32": 4}[batch.dtype]
     ob = 4 if batch.dtype == "f32" else 2
-    return float(batch.total * batch.hq * D * (eb + ob) + 2 * batch.total * batch.hkv * D * eb)
+    return float(batch.total * batch.hq * D * (eb + ob) + 2 * batch.total_kv * batch.hkv * D * eb)
 
 
-def csr_work(lengths, hq, hkv, cu, idx, correction):
+def csr_work(lengths, hq, hkv, cu, idx, correction, q_lengths=None):
     """Algorithmic and executed attention FLOPs of a CSR (host arithmetic on the index).
 
     algorithmic: 4 d per (packed row, visible key in a listed tile) + 4 d per
     (packed row, corrected block); executed: 4 d x 128 rows x 64 per step the
-    kernel runs (listed tiles + correction chunks with something to correct)."""
+    kernel runs (listed tiles + correction chunks with something to correct).
+    Queries sit at positions L - L_q .. L - 1 of their request."""
     g = hq // hkv
+    q_lengths = lengths if q_lengths is None else q_lengths
     alg = 0.0
     steps = 0
     nsel_blocks = 0
     ncand = 0
     s = 0
-    for L in lengths:
-        nt = -(-g * L // 128)
+    for L, Lq in zip(lengths, q_lengths):
+        nt = -(-g * Lq // 128)
+        off = L - Lq
         for h in range(hkv):
             for I in range(nt):
-                r0, r1 = I * 128, min((I + 1) * 128, g * L)
-                pos = np.arange(r0, r1) // g
-                t0 = r0 // g
-                beta = t0 // 128
+                r0, r1 = I * 128, min((I + 1) * 128, g * Lq)
+                pos = off + np.arange(r0, r1) // g
+                t0, t1 = int(pos[0]), int(pos[-1])
+                beta, beta1 = t0 // 128, t1 // 128
                 lst = idx[cu[s]:cu[s + 1]]
                 full = int(np.count_nonzero(lst < 2 * beta))
                 keys = 64 * full + np.zeros(len(pos))
-                for p in (2 * beta, 2 * beta + 1):
-                    if np.any(lst == p):
-                        keys += np.clip(pos - 64 * p + 1, 0, 64)
+                for p in lst[lst >= 2 * beta]:
+                    keys += np.clip(pos - 64 * int(p) + 1, 0, 64)
                 blocks = np.unique(lst // 2)
                 sel_before = int(np.count_nonzero(blocks < beta))
                 corr = (beta - sel_before) if correction else 0
@@ -83,7 +92,7 @@ def csr_work(lengths, hq, hkv, cu, idx, correction):
                             st += 1
                 steps += st
                 nsel_blocks += len(blocks)
-                ncand += beta + 1
+                ncand += beta1 + 1
                 s += 1
     execd = 4.0 * D * 128 * 64 * steps
     return alg, execd, nsel_blocks / max(1, ncand)
@@ -121,21 +130,28 @@ def time_calls(fn, steps, warmup):
 
 
 class Case:
-    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4):
+    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4, dev=None):
+        """``dev``: (q, k, v) already on the device (views are fine), else uploaded."""
         from block_sparse_long_mean_amd import fp
 
         self.fp = fp
         self.batch = batch
         tdt = {"bf16": torch.bfloat16, "e4m3": torch.uint8, "f32": torch.float32}[batch.dtype]
-        self.q = batch.q.cuda()
-        if paged is None:
+        if dev is not None:
+            self.q, self.k, self.v = dev
+            self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt, cu_seqlens_kv=batch.cu_kv,
+                                   descale=batch.descale if batch.dtype == "e4m3" else None)
+        elif paged is None:
+            self.q = batch.q.cuda()
             self.k, self.v = batch.k.cuda(), batch.v.cuda()
-            self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt,
+            self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt, cu_seqlens_kv=batch.cu_kv,
                                    descale=batch.descale if batch.dtype == "e4m3" else None)
         else:
+            self.q = batch.q.cuda()
             self.k, self.v = paged.k_pool.cuda(), paged.v_pool.cuda()
             self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt, page_table=paged.page_table,
                                    page_size=paged.page_size, num_pool_slots=paged.num_slots,
+                                   cu_seqlens_kv=batch.cu_kv,
                                    descale=batch.descale if batch.dtype == "e4m3" else None)
         self.params = fp.select_params(alpha, sink, win)
         self.bufs = fp.Buffers(self.B, self.params)
@@ -164,7 +180,7 @@ def measure(case, steps, warmup, correction=True):
     att = time_calls(lambda: case.attn(correction), steps, warmup)
     cu, idx = case.csr()
     b = case.batch
-    alg, execd, density = csr_work(b.lengths, b.hq, b.hkv, cu, idx, correction)
+    alg, execd, density = csr_work(b.lengths, b.hq, b.hkv, cu, idx, correction, b.q_lengths)
     sel_ms, att_ms = float(np.median(sel)), float(np.median(att))
     return {"select_ms": sel_ms, "attn_ms": att_ms, "step_ms": sel_ms + att_ms, "density": density,
             "attn_alg_flop": alg, "attn_exec_flop": execd, "csr_entries": int(len(idx)),
@@ -198,8 +214,9 @@ def cpu_baseline(batch, w, n_seg=64):
     flops = 0.0
     for s in segs:
         b, _, _ = P.segment_coords(s)
-        pos, _, valid = P.rows_of_segment(s)
-        flops += float(np.sum(4.0 * D * (pos[valid] - P.cu[b] + 1)))
+        rows, _, valid = P.rows_of_segment(s)
+        off = batch.lengths[b] - batch.q_lengths[b]
+        flops += float(np.sum(4.0 * D * (off + rows[valid] - P.cu[b] + 1)))
     # dense-equivalent rate of the sampled rows, charging the pooling pro rata
     total_rows = batch.total * batch.hq
     sample_rows = n_seg * 128
@@ -219,7 +236,7 @@ def sweep(args):
         case = Case(batch, None, w.alpha, w.sink_blocks, w.window_blocks)
         m = measure(case, max(3, args.steps // 2), max(1, args.warmup))
         d_ms = float(np.median(time_calls(case.dense, 3, 1)))
-        F = dense_flops(batch.lengths, batch.hq)
+        F = dense_flops(batch.lengths, batch.hq, batch.q_lengths)
         print(json.dumps({
             "sweep": w.name, "L": batch.lengths[0], "num_reqs": len(batch.lengths),
             "select_ms": m["select_ms"], "attn_ms": m["attn_ms"], "step_ms": m["step_ms"],
@@ -228,6 +245,44 @@ def sweep(args):
             "eff_tflops": F / (m["step_ms"] / 1e3) / 1e12,
             "attn_alg_tflops": m["attn_alg_flop"] / (m["attn_ms"] / 1e3) / 1e12}), flush=True)
         del case, batch
+        torch.cuda.empty_cache()
+
+
+def chunked(args):
+    """The 128K prompt of the headline layer prefilled in chunks of 8K and 16K
+    tokens, the index rebuilt for every chunk: per chunk size, the summed select,
+    attention and dense-baseline times over all chunks, next to the same prompt
+    in one pass.  One JSON line per chunk size."""
+    w = configs.L128K
+    batch, _ = w.make()
+    L = batch.lengths[0]
+    dq, dk, dv = batch.q.cuda(), batch.k.cuda(), batch.v.cuda()
+    reps, warm = max(3, args.steps // 2), max(1, args.warmup)
+    whole = Case(batch, None, w.alpha, w.sink_blocks, w.window_blocks, dev=(dq, dk, dv))
+    m = measure(whole, reps, warm)
+    whole_dense = float(np.median(time_calls(whole.dense, 3, 1)))
+    del whole
+    for C in (8192, 16384):
+        tot = {"select_ms": 0.0, "attn_ms": 0.0, "dense_ms": 0.0, "alg": 0.0, "sel": 0.0, "cand": 0.0}
+        for stop in range(C, L + 1, C):
+            ch = synth.prefix_chunk(batch, stop, C)
+            case = Case(ch, None, w.alpha, w.sink_blocks, w.window_blocks,
+                        dev=(dq[stop - C:stop], dk[:stop], dv[:stop]))
+            mc = measure(case, reps, warm)
+            tot["select_ms"] += mc["select_ms"]
+            tot["attn_ms"] += mc["attn_ms"]
+            tot["dense_ms"] += float(np.median(time_calls(case.dense, 3, 1)))
+            tot["alg"] += mc["attn_alg_flop"]
+            del case
+        step = tot["select_ms"] + tot["attn_ms"]
+        print(json.dumps({
+            "chunked": w.name, "chunk": C, "n_chunks": L // C,
+            "select_ms": tot["select_ms"], "attn_ms": tot["attn_ms"], "step_ms": step,
+            "dense_ms": tot["dense_ms"], "speedup_vs_dense": tot["dense_ms"] / step,
+            "select_share": tot["select_ms"] / step,
+            "attn_alg_tflops": tot["alg"] / (tot["attn_ms"] / 1e3) / 1e12,
+            "unchunked_step_ms": m["step_ms"], "unchunked_dense_ms": whole_dense,
+            "unchunked_speedup_vs_dense": whole_dense / m["step_ms"]}), flush=True)
         torch.cuda.empty_cache()
 
 
@@ -245,6 +300,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="length sweep 4K..128K at 4 requests: one JSON line per length (select, attention, "
                          "dense baseline, speedup, density)")
+    ap.add_argument("--chunked", action="store_true",
+                    help="the 128K prompt in 8K and 16K chunks (index rebuilt per chunk) against one pass: "
+                         "one JSON line per chunk size")
     args = ap.parse_args()
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -260,6 +318,9 @@ def main():
     if args.sweep:
         sweep(args)
         return
+    if args.chunked:
+        chunked(args)
+        return
 
     w = configs.ALL[args.config]
     t0 = time.time()
@@ -267,7 +328,7 @@ def main():
     gen_s = time.time() - t0
     case = Case(batch, paged, w.alpha, w.sink_blocks, w.window_blocks)
     main_m = measure(case, args.steps, args.warmup, correction=True)
-    F = dense_flops(batch.lengths, batch.hq)
+    F = dense_flops(batch.lengths, batch.hq, batch.q_lengths)
     peak = PEAK[batch.dtype]
     attn_s = main_m["attn_ms"] / 1e3
     achieved = main_m["attn_alg_flop"] / attn_s / 1e12
@@ -318,6 +379,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": batch.dtype, "data": "synthetic (seeded generator standing in for RULER needle-in-a-haystack)",
         "config": {"workload": w.name, "lengths": list(batch.lengths)[:4] + (["..."] if len(batch.lengths) > 4 else []),
+                   "q_lengths": None if not batch.chunked else list(batch.q_lengths)[:4] + (
+                       ["..."] if len(batch.q_lengths) > 4 else []),
                    "num_reqs": len(batch.lengths), "hq": batch.hq, "hkv": batch.hkv, "d": D, "alpha": w.alpha,
                    "sink_blocks": w.sink_blocks, "window_blocks": w.window_blocks,
                    "paged": bool(w.page_size), "mean_correction": True},

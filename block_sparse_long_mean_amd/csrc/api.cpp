@@ -33,10 +33,10 @@ fp_status fail(fp_status s, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Host view of the batch, derived from cu_seqlens_q_host only.
+// Host view of the batch, derived from the host copies of the offsets.
 struct HostGeo {
-  int64_t total = 0, n_seg = 0, nb_pad = 0, idx_cap = 0;
-  int32_t max_len = 0, max_nj = 1, words = 1, g = 1, log2g = 0;
+  int64_t total = 0, total_kv = 0, n_seg = 0, nb_pad = 0, idx_cap = 0;
+  int32_t max_len = 0, max_nj = 1, words = 1, g = 1, log2g = 0;  // max_len: longest K/V sequence
 };
 
 fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
@@ -59,31 +59,39 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale >= 0.f))
     return fail(FP_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   const int32_t* cu = p->cu_seqlens_q_host;
+  if ((p->cu_seqlens_kv == nullptr) != (p->cu_seqlens_kv_host == nullptr))
+    return fail(FP_ERR_INVALID_ARG, "cu_seqlens_kv and cu_seqlens_kv_host are given together or not at all");
+  const int32_t* ckv = p->cu_seqlens_kv_host ? p->cu_seqlens_kv_host : cu;
   if (cu[0] != 0) return fail(FP_ERR_INVALID_ARG, "cu_seqlens_q_host[0] must be 0");
+  if (ckv[0] != 0) return fail(FP_ERR_INVALID_ARG, "cu_seqlens_kv_host[0] must be 0");
   hg->g = g;
   while ((1 << hg->log2g) < g) ++hg->log2g;
   int64_t max_len = 0;
   for (int b = 0; b < p->num_reqs; ++b) {
-    int64_t L = (int64_t)cu[b + 1] - cu[b];
-    if (L < 0) return fail(FP_ERR_INVALID_ARG, "cu_seqlens_q_host decreases at request %d", b);
+    const int64_t Lq = (int64_t)cu[b + 1] - cu[b];
+    const int64_t L = (int64_t)ckv[b + 1] - ckv[b];
+    if (Lq < 0) return fail(FP_ERR_INVALID_ARG, "cu_seqlens_q_host decreases at request %d", b);
+    if (L < Lq)
+      return fail(FP_ERR_INVALID_ARG, "request %d has %lld keys for %lld queries (needs L_kv >= L_q)", b,
+                  (long long)L, (long long)Lq);
     if (L > (int64_t)kMaxBlocks * kBlock)
       return fail(FP_ERR_UNSUPPORTED, "request %d has %lld tokens; the limit is %d", b, (long long)L,
                   kMaxBlocks * kBlock);
     max_len = std::max(max_len, L);
-    const int64_t nt = ((L << hg->log2g) + kRows - 1) / kRows;
+    const int64_t off = L - Lq;  // position of the request's first query
+    const int64_t nt = ((Lq << hg->log2g) + kRows - 1) / kRows;
     hg->n_seg += (int64_t)p->num_heads_kv * nt;
     const int64_t nj = (L + kBlock - 1) / kBlock;
     hg->nb_pad += (nj + kChunk - 1) / kChunk * kChunk;
     // worst-case CSR: every causal tile of every segment
     for (int64_t I = 0; I < nt; ++I) {
-      int64_t t0 = (I * kRows) >> hg->log2g;
-      int64_t r1 = std::min((I + 1) * kRows, L << hg->log2g);
-      int64_t t1 = (r1 - 1) >> hg->log2g;
-      (void)t0;
+      int64_t r1 = std::min((I + 1) * kRows, Lq << hg->log2g);
+      int64_t t1 = off + ((r1 - 1) >> hg->log2g);
       hg->idx_cap += (int64_t)p->num_heads_kv * (t1 / kTile + 1);
     }
   }
   hg->total = cu[p->num_reqs];
+  hg->total_kv = ckv[p->num_reqs];
   if (hg->total > INT32_MAX / 2) return fail(FP_ERR_UNSUPPORTED, "total_q too large");
   if (hg->n_seg > INT32_MAX / 16 || hg->idx_cap > INT32_MAX)
     return fail(FP_ERR_UNSUPPORTED, "too many segments for int32 CSR offsets");
@@ -185,6 +193,7 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
 Geo make_geo(const fp_problem* p, const HostGeo& hg, char* ws, const WsLayout& wl) {
   Geo g{};
   g.cu_q = p->cu_seqlens_q;
+  g.cu_kv = p->cu_seqlens_kv ? p->cu_seqlens_kv : p->cu_seqlens_q;
   g.page_table = p->page_table;
   g.num_slots = p->page_table ? p->num_pool_slots : 0;
   g.page_size = p->page_table ? p->page_size : 1;
@@ -270,9 +279,10 @@ fp_status fp_query_sizes(const fp_problem* prob, const fp_select_params* params,
 
 int64_t fp_block_base(const fp_problem* prob, int32_t b) {
   if (!prob || !prob->cu_seqlens_q_host || b < 0 || b >= prob->num_reqs) return -1;
+  const int32_t* ckv = prob->cu_seqlens_kv_host ? prob->cu_seqlens_kv_host : prob->cu_seqlens_q_host;
   int64_t base = 0;
   for (int i = 0; i < b; ++i) {
-    int64_t L = (int64_t)prob->cu_seqlens_q_host[i + 1] - prob->cu_seqlens_q_host[i];
+    int64_t L = (int64_t)ckv[i + 1] - ckv[i];
     base += ((L + kBlock - 1) / kBlock + kChunk - 1) / kChunk * kChunk;
   }
   return base;
@@ -284,7 +294,7 @@ fp_status fp_pool(const fp_problem* prob, const void* k, const void* v, void* me
   fp_status s = prepare(prob, ws, ws_bytes, &pr);
   if (s != FP_OK) return s;
   if (!k || !v || !means) return fail(FP_ERR_INVALID_ARG, "k, v and means are required");
-  if (pr.hg.total == 0) return FP_OK;
+  if (pr.hg.total_kv == 0) return FP_OK;
   hipStream_t st = (hipStream_t)stream;
   FP_LAUNCH(launch_meta(pr.g, st));
   FP_LAUNCH(launch_pool(pr.g, pr.ml, k, v, (char*)means, st));

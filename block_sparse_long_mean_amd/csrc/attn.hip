@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     } else {
       seg0 = cu[un.s];
       T = cu[un.s + 1] - seg0;
-      if (T < 0 || T > 2 * (t.beta + 1)) {
+      if (T < 0 || T > 2 * (t.beta1 + 1)) {
         err |= kErrIdx;
         T = 0;
       }
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const char* vbase;
     uint64_t kvbytes;
     if constexpr (AM == kContig) {
-      const uint64_t base = ((uint64_t)c.row0 * g.hkv + c.h) * kD * EB;
+      const uint64_t base = ((uint64_t)c.kv0 * g.hkv + c.h) * kD * EB;
       kbase = (const char*)k + base;
       vbase = (const char*)v + base;
       kvbytes = c.L > 0 ? (uint64_t)(c.L - 1) * rowstride + kD * EB : 0;
@@ -423,9 +423,10 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const int row_in_tile = wave * 32 + col;
     const bool row_ok = row_in_tile < t.nrows;
     const int64_t prow = c.I * kRows + row_in_tile;
-    const int pos = (int)(prow >> g.log2g);
+    const int qi = (int)(prow >> g.log2g);  // query index within the request
+    const int pos = c.off + qi;             // its position (causal mask)
     const int head = c.h * g.g + (int)(prow & (g.g - 1));
-    const int64_t qrow = (c.row0 + pos) * g.hq + head;
+    const int64_t qrow = (c.row0 + qi) * g.hq + head;
     Op qf[C::NM0];
 #pragma unroll
     for (int m = 0; m < C::NM0; ++m) {
@@ -1229,7 +1230,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               }
             }
           if (lse && half == 0)
-            lse[(c.row0 + pos) * g.hq + head] =
+            lse[(c.row0 + qi) * g.hq + head] =
                 (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
         } else {
 #pragma unroll
@@ -1242,7 +1243,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               else
                 *(uint2*)((uint16_t*)out + qrow * kD + n0) = make_uint2(kNaNbf16x2, kNaNbf16x2);
             }
-          if (lse && half == 0) ((uint32_t*)lse)[(c.row0 + pos) * g.hq + head] = kNaN32;
+          if (lse && half == 0) ((uint32_t*)lse)[(c.row0 + qi) * g.hq + head] = kNaN32;
         }
       }
     } else {
@@ -1306,9 +1307,9 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
   const float cvs = DT == kE4M3 ? g.descale[2] : 1.f;
   const float inv = cvs / L;
   const int64_t prow = c.I * kRows + r;
-  const int pos = (int)(prow >> g.log2g);
+  const int qi = (int)(prow >> g.log2g);  // query index within the request
   const int head = c.h * g.g + (int)(prow & (g.g - 1));
-  const int64_t qrow = (c.row0 + pos) * g.hq + head;
+  const int64_t qrow = (c.row0 + qi) * g.hq + head;
   for (int n = n0; n < n0 + 64; n += 4) {
     float a[4] = {0.f, 0.f, 0.f, 0.f};
     for (int u = 0; u < U; ++u) {
@@ -1328,7 +1329,7 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
   }
   if (lse && n0 == 0) {
     constexpr float kOffL = DT == kE4M3 ? 8.f : 0.f;
-    lse[(c.row0 + pos) * g.hq + head] = (Mu + __builtin_amdgcn_logf(L) - kOffL) * 0.6931471805599453f;
+    lse[(c.row0 + qi) * g.hq + head] = (Mu + __builtin_amdgcn_logf(L) - kOffL) * 0.6931471805599453f;
   }
 }
 

@@ -75,8 +75,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 struct SegCoord {
   int b, h;
   int64_t I;
-  int L;        // request length
+  int L;        // key/value length of the request
+  int Lq;       // query length (the queries are the last Lq positions)
+  int off;      // position of the first query: L - Lq
   int64_t row0; // first Q row of the request
+  int64_t kv0;  // first K/V row of the request (contiguous layout)
 };
 
 __device__ __forceinline__ SegCoord seg_coord(const Geo& g, int64_t s) {
@@ -96,33 +99,41 @@ __device__ __forceinline__ SegCoord seg_coord(const Geo& g, int64_t s) {
   c.h = (int)(local / nt);
   c.I = local - (int64_t)c.h * nt;
   c.row0 = g.cu_q[lo];
-  c.L = g.cu_q[lo + 1] - g.cu_q[lo];
+  c.Lq = g.cu_q[lo + 1] - g.cu_q[lo];
+  c.kv0 = g.cu_kv[lo];
+  c.L = g.cu_kv[lo + 1] - g.cu_kv[lo];
+  c.off = c.L - c.Lq;
   return c;
 }
 
-// Tile geometry: valid packed rows, first/last position and the tile's block.
+// Tile geometry: valid packed rows, first/last (absolute) position, and the
+// blocks of the first and last position.  Packed row r of the tile is query
+// r >> log2g of the request, at position off + (r >> log2g).  A fresh prefill's
+// tile never crosses a block edge (beta1 == beta); a chunk that starts inside a
+// block can put one tile across two blocks, and both are its diagonal.
 struct TileGeo {
   int nrows;
-  int t0, t1, beta;
+  int t0, t1, beta, beta1;
 };
 
 __device__ __forceinline__ TileGeo tile_geo(const Geo& g, const SegCoord& c) {
   TileGeo t;
-  int64_t packed = (int64_t)c.L << g.log2g;
+  int64_t packed = (int64_t)c.Lq << g.log2g;
   int64_t r0 = c.I * kRows;
   int64_t r1 = r0 + kRows;
   if (r1 > packed) r1 = packed;
   t.nrows = (int)(r1 - r0);
-  t.t0 = (int)(r0 >> g.log2g);
-  t.t1 = (int)((r1 - 1) >> g.log2g);
+  t.t0 = c.off + (int)(r0 >> g.log2g);
+  t.t1 = c.off + (int)((r1 - 1) >> g.log2g);
   t.beta = t.t0 / kBlock;
+  t.beta1 = t.t1 / kBlock;
   return t;
 }
 
 // Row of the K/V storage holding token j of request b ([V2] Eq. 22), or -1
 // when the page table points outside the pool.
 __device__ __forceinline__ int64_t kv_row(const Geo& g, const SegCoord& c, int j) {
-  if (!g.page_table) return c.row0 + j;
+  if (!g.page_table) return c.kv0 + j;
   int pg = j / g.page_size;
   int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
   int64_t slot = page * g.page_size + (j - pg * g.page_size);

@@ -38,7 +38,8 @@ struct WsHeader {
 
 // Everything a kernel needs to walk the batch.  Passed by value.
 struct Geo {
-  const int32_t* cu_q;        // [nreq+1]
+  const int32_t* cu_q;        // [nreq+1] query rows
+  const int32_t* cu_kv;       // [nreq+1] key/value offsets (== cu_q for a fresh prefill)
   const int32_t* page_table;  // nullable
   int64_t num_slots;
   int32_t page_size;

@@ -21,9 +21,11 @@ __global__ __launch_bounds__(1024) void meta_kernel(Geo g) {
   const int lo = tid * per;
   const int hi = min(lo + per, g.nreq);
   int64_t ns = 0, nb = 0;
+  // segments come from the query length, blocks from the key length
   for (int b = lo; b < hi; ++b) {
-    int64_t L = g.cu_q[b + 1] - g.cu_q[b];
-    ns += (int64_t)g.hkv * (((L << g.log2g) + kRows - 1) / kRows);
+    int64_t Lq = g.cu_q[b + 1] - g.cu_q[b];
+    int64_t L = g.cu_kv[b + 1] - g.cu_kv[b];
+    ns += (int64_t)g.hkv * (((Lq << g.log2g) + kRows - 1) / kRows);
     nb += ((L + kBlock - 1) / kBlock + kChunk - 1) / kChunk * kChunk;
   }
   sseg[tid] = ns;
@@ -41,8 +43,9 @@ __global__ __launch_bounds__(1024) void meta_kernel(Geo g) {
   for (int b = lo; b < hi; ++b) {
     g.seg_off[b] = (int32_t)s0;
     g.blk_base[b] = (int32_t)b0;
-    int64_t L = g.cu_q[b + 1] - g.cu_q[b];
-    s0 += (int64_t)g.hkv * (((L << g.log2g) + kRows - 1) / kRows);
+    int64_t Lq = g.cu_q[b + 1] - g.cu_q[b];
+    int64_t L = g.cu_kv[b + 1] - g.cu_kv[b];
+    s0 += (int64_t)g.hkv * (((Lq << g.log2g) + kRows - 1) / kRows);
     b0 += ((L + kBlock - 1) / kBlock + kChunk - 1) / kChunk * kChunk;
   }
   if (tid == 1023) {
@@ -98,7 +101,10 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
   c.h = h;
   c.I = 0;
   c.row0 = g.cu_q[lo];
-  c.L = g.cu_q[lo + 1] - g.cu_q[lo];
+  c.Lq = g.cu_q[lo + 1] - g.cu_q[lo];
+  c.kv0 = g.cu_kv[lo];
+  c.L = g.cu_kv[lo + 1] - g.cu_kv[lo];
+  c.off = c.L - c.Lq;
   const int J = (int)(gb - g.blk_base[lo]);
   const int n = max(0, min(kBlock, c.L - J * kBlock));
   const float ck = DT == kE4M3 ? g.descale[1] : 1.f;

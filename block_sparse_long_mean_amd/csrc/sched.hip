@@ -29,7 +29,7 @@ __device__ __forceinline__ void seg_work(const Geo& g, const int32_t* cu, int64_
     W = t.t1 / kTile + 1;
   } else {
     int T = cu[s + 1] - cu[s];
-    T = max(0, min(T, 2 * (t.beta + 1)));
+    T = max(0, min(T, 2 * (t.beta1 + 1)));
     W = T + (correction ? (t.beta + kChunk - 1) / kChunk : 0);
   }
   W = max(W, 1);

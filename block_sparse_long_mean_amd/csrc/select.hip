@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   const float sl = g.scale * 1.4426950408889634f * (DT == kE4M3 ? g.descale[0] : 1.f);
-  const int nc = t.beta + 1;
+  const int nc = t.beta1 + 1;  // blocks holding a key visible to some row
   const int njt = (nc + 31) >> 5;
   const bf16x8* khi = (const bf16x8*)(means + ml.khi);
   const bf16x8* klo = (const bf16x8*)(means + ml.klo);
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   for (int base = wave * 64; base < nc; base += 256) {
     const int J = base + lane;
     const bool in = J < nc;
-    const bool forced = J < sink || (J >= t.beta - win && J < t.beta) || J == t.beta;
+    const bool forced = J < sink || (J >= t.beta - win && J < t.beta) || J >= t.beta;
     const bool sel = in && (forced || SJ[J] >= thr);
     const uint64_t m = __ballot(sel);
     if (lane == 0) {
@@ -270,9 +270,9 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   __syncthreads();
   if (threadIdx.x == 0) {
     int tot = nsel_w[0] + nsel_w[1] + nsel_w[2] + nsel_w[3];
-    // each kept block gives tiles 2J and 2J+1; the diagonal block's second tile
-    // is dropped when it starts after the tile's last position
-    int trim = (int64_t)kTile * (2 * t.beta + 1) > t.t1 ? 1 : 0;
+    // each kept block gives tiles 2J and 2J+1; the last block's second tile is
+    // dropped when it starts after the tile's last position
+    int trim = (int64_t)kTile * (2 * t.beta1 + 1) > t.t1 ? 1 : 0;
     counts[s] = 2 * tot - trim;
   }
 }
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void expand_kernel(Geo g, const int32_t* __res
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
   const int64_t start = cu[s];
-  const int nc = t.beta + 1;
+  const int nc = t.beta1 + 1;  // blocks holding a key visible to some row
   int o = 0;
   for (int base = 0; base < nc; base += 64) {
     const int J = base + lane;

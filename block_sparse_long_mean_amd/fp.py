@@ -36,6 +36,7 @@ class Problem(C.Structure):
         ("page_table", C.c_void_p), ("page_size", C.c_int32), ("max_pages_per_req", C.c_int32),
         ("num_pool_slots", C.c_int64), ("dtype", C.c_int32), ("descale", C.c_void_p),
         ("softmax_scale", C.c_float),
+        ("cu_seqlens_kv", C.c_void_p), ("cu_seqlens_kv_host", C.c_void_p),
     ]
 
 
@@ -107,6 +108,8 @@ class Batch:
     cu_host: np.ndarray
     page_table: torch.Tensor | None
     descale: torch.Tensor | None
+    cu_kv_dev: torch.Tensor | None = None
+    cu_kv_host: np.ndarray | None = None
 
     @property
     def ptr(self):
@@ -114,11 +117,17 @@ class Batch:
 
 
 def make_batch(cu_seqlens, num_heads_q, num_heads_kv, dtype, device="cuda", head_dim=128,
-               page_table=None, page_size=0, num_pool_slots=0, descale=None, softmax_scale=0.0) -> Batch:
-    """Build the C problem struct.  ``cu_seqlens`` is a host sequence; ``dtype`` a torch dtype
-    (float32, bfloat16, or uint8 for E4M3 codes); ``page_table`` a host int array or None."""
+               page_table=None, page_size=0, num_pool_slots=0, descale=None, softmax_scale=0.0,
+               cu_seqlens_kv=None) -> Batch:
+    """Build the C problem struct.  ``cu_seqlens`` (query rows) and ``cu_seqlens_kv`` (K/V
+    lengths; None = the same) are host sequences; ``dtype`` a torch dtype (float32, bfloat16,
+    or uint8 for E4M3 codes); ``page_table`` a host int array or None."""
     cu_host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     cu_dev = torch.from_numpy(cu_host.copy()).to(device)
+    kv_host = kv_dev = None
+    if cu_seqlens_kv is not None:
+        kv_host = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int32))
+        kv_dev = torch.from_numpy(kv_host.copy()).to(device)
     pt = None
     max_pages = 0
     if page_table is not None:
@@ -130,8 +139,9 @@ def make_batch(cu_seqlens, num_heads_q, num_heads_kv, dtype, device="cuda", head
         ds = torch.tensor(list(descale), dtype=torch.float32, device=device)
     prob = Problem(len(cu_host) - 1, num_heads_q, num_heads_kv, head_dim, cu_dev.data_ptr(),
                    cu_host.ctypes.data, _ptr(pt), page_size if pt is not None else 0, max_pages,
-                   num_pool_slots if pt is not None else 0, _DT[dtype], _ptr(ds), softmax_scale)
-    return Batch(prob, cu_dev, cu_host, pt, ds)
+                   num_pool_slots if pt is not None else 0, _DT[dtype], _ptr(ds), softmax_scale,
+                   _ptr(kv_dev), None if kv_host is None else kv_host.ctypes.data)
+    return Batch(prob, cu_dev, cu_host, pt, ds, kv_dev, kv_host)
 
 
 def select_params(alpha=0.1, sink_blocks=2, window_blocks=4, block_size=128) -> SelectParams:

@@ -31,7 +31,8 @@
  *     fp_read_device_error reports it.
  *   - Layouts (row-major, element = head_dim-vector):
  *       Q, O     [total_q][num_heads_q][head_dim], rows ragged by cu_seqlens_q
- *       K, V     contiguous: [total_q][num_heads_kv][head_dim] (same rows as Q)
+ *       K, V     contiguous: [total_kv][num_heads_kv][head_dim], rows ragged by
+ *                cu_seqlens_kv (by cu_seqlens_q when that is NULL)
  *                paged:      [num_pool_slots][num_heads_kv][head_dim]; token j of
  *                request b lives in slot page_table[b][j/p]*p + j%p ([V2] Eq. 22)
  *       LSE      [total_q][num_heads_q] float, natural log
@@ -72,22 +73,31 @@ typedef enum {
 typedef enum { FP_F32 = 0, FP_BF16 = 1, FP_E4M3 = 2 } fp_dtype;
 
 /* One batch of prefill requests.  Built once per forward step and shared by
- * every layer ([V2] §3.4, serving integration).  Query and KV lengths are
- * equal (fresh prefill, no cached prefix). */
+ * every layer ([V2] §3.4, serving integration).  A request has L_kv keys and
+ * L_q <= L_kv queries; the queries are its last L_q positions, i.e. query i
+ * sits at position L_kv - L_q + i: a prefill chunk over a cached prefix, with
+ * the index re-run for every chunk ([V2] §4.3 "Compatibility with Chunked
+ * Prefill").  Leaving both cu_seqlens_kv pointers NULL means L_kv = L_q
+ * (fresh prefill). */
 typedef struct {
   int32_t num_reqs;              /* >= 1 */
   int32_t num_heads_q;           /* multiple of num_heads_kv */
   int32_t num_heads_kv;          /* >= 1; g = num_heads_q/num_heads_kv is a power of 2 <= 128 */
   int32_t head_dim;              /* must be 128 */
-  const int32_t* cu_seqlens_q;   /* [num_reqs+1] row offsets of Q/O (and contiguous K/V) */
+  const int32_t* cu_seqlens_q;   /* [num_reqs+1] row offsets of Q/O (and of contiguous K/V when
+                                    cu_seqlens_kv is NULL) */
   const int32_t* cu_seqlens_q_host; /* (host) the same values; sizes grids, checked for order */
   const int32_t* page_table;     /* [num_reqs][max_pages_per_req] page ids, or NULL = contiguous */
   int32_t page_size;             /* p >= 1, any value ([V2] Eq. 22); ignored when contiguous */
-  int32_t max_pages_per_req;     /* row stride of page_table; >= ceil(max length / p) */
+  int32_t max_pages_per_req;     /* row stride of page_table; >= ceil(max L_kv / p) */
   int64_t num_pool_slots;        /* rows of the paged K/V pool; ignored when contiguous */
   int32_t dtype;                 /* fp_dtype of Q, K and V */
   const float* descale;          /* [3] = {c_q, c_k, c_v} for FP_E4M3, else NULL */
   float softmax_scale;           /* sigma; 0 means 1/sqrt(head_dim) */
+  const int32_t* cu_seqlens_kv;  /* [num_reqs+1] K/V lengths as offsets (rows of contiguous K/V),
+                                    or NULL: the same as cu_seqlens_q */
+  const int32_t* cu_seqlens_kv_host; /* (host) the same values, or NULL; given together with
+                                        cu_seqlens_kv; every L_kv >= its L_q */
 } fp_problem;
 
 /* Block selection settings ([V2] §3.1 Eq. 3, §3.3 Eq. 20, defaults in §4.1:
@@ -117,7 +127,7 @@ fp_status fp_query_sizes(const fp_problem* prob, const fp_select_params* params,
  * are descaled first.  Writes `means` (means_bytes).  Its first two arrays are
  * float kbar and vbar, [NB][num_heads_kv][head_dim] each, where request b's
  * blocks start at block fp_block_base(b) = sum over earlier requests of
- * ceil(ceil(L/128)/64)*64; the rest of the buffer holds derived operand
+ * ceil(ceil(L_kv/128)/64)*64; the rest of the buffer holds derived operand
  * copies private to the library.  fp_select calls this itself. */
 fp_status fp_pool(const fp_problem* prob, const void* k, const void* v, void* means, void* ws,
                   size_t ws_bytes, void* stream);
@@ -161,7 +171,7 @@ fp_status fp_dense_attn(const fp_problem* prob, const void* q, const void* k, co
 fp_status fp_read_device_error(void* ws, void* stream, int32_t* flag /* (host) */);
 
 /* First block of request b in the pooled-statistics arrays (host arithmetic
- * on cu_seqlens_q_host); -1 if b is out of range. */
+ * on the K/V lengths); -1 if b is out of range. */
 int64_t fp_block_base(const fp_problem* prob, int32_t b);
 
 const char* fp_status_string(fp_status s);

@@ -4,6 +4,7 @@ import ctypes as C
 import math
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -152,3 +153,48 @@ def test_calls_fail_before_launch_on_small_buffers():
     r = lib.fp_dense_attn(C.byref(p), dummy, dummy, dummy, dummy, None, None, s.workspace_bytes, None)
     assert r == -1
     assert lib.fp_status_string(-3) == b"workspace too small"
+
+
+def test_chunked_problem_geometry_and_checks():
+    """K/V lengths from cu_seqlens_kv: segments from the queries, blocks and the
+    worst-case CSR from the keys (queries at positions L_kv - L_q ..)."""
+    fp = _fp()
+    p, cu = _problem(fp, lengths=(1000, 300))
+    ckv = np.array([0, 3000, 3300], np.int32)
+    p.cu_seqlens_kv = 0x2000  # never dereferenced on the host
+    p.cu_seqlens_kv_host = ckv.ctypes.data
+    st, s = _sizes(fp, p, fp.select_params())
+    assert st == 0, fp.lib_handle().fp_last_error()
+    g = 8
+    assert s.n_segments == 4 * (math.ceil(g * 1000 / 128) + math.ceil(g * 300 / 128))
+    assert s.max_blocks == math.ceil(3000 / 128)
+    cap = 0
+    for L, Lq in ((3000, 1000), (300, 300)):
+        for I in range(math.ceil(g * Lq / 128)):
+            t1 = L - Lq + (min((I + 1) * 128, g * Lq) - 1) // g
+            cap += 4 * (t1 // 64 + 1)
+    assert s.idx_capacity == cap
+    assert fp.lib_handle().fp_block_base(C.byref(p), 1) == 64  # ceil(24 / 64) * 64
+    # fewer keys than queries
+    ckv[1] = 999
+    assert _sizes(fp, p)[0] == -1
+    ckv[1] = 3000
+    # the two K/V offset pointers go together
+    p.cu_seqlens_kv_host = None
+    assert _sizes(fp, p)[0] == -1
+
+
+def test_problem_struct_matches_the_header(tmp_path):
+    """The binding's ctypes layout of fp_problem equals the C compiler's."""
+    fp = _fp()
+    src = tmp_path / "lay.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "fp.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu\\n", sizeof(fp_problem),'
+                   ' offsetof(fp_problem, softmax_scale), offsetof(fp_problem, cu_seqlens_kv),'
+                   ' offsetof(fp_problem, cu_seqlens_kv_host)); return 0;}\n')
+    exe = tmp_path / "lay"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)])
+    got = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    P = fp.Problem
+    assert got == [C.sizeof(P), P.softmax_scale.offset, P.cu_seqlens_kv.offset,
+                   P.cu_seqlens_kv_host.offset]

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 from block_sparse_long_mean_amd import configs
-from tests.gpu_harness import GpuRun, compare_attn, compare_csr, oracle_for, sample_segments
+from tests.gpu_harness import GpuRun, check_e4m3, compare_attn, compare_csr, oracle_for, sample_segments
 
 pytestmark = pytest.mark.gpu
 
@@ -48,18 +48,13 @@ def _check_pool(run, P):
 
 def _attn_check(run, P, segs, cu, idx, dtype, correction=True):
     out, lse = run.attn(correction=correction)
-    mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=correction)
-    _note(f"  attention corr={correction}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
     tmax, tmean = TOL[dtype]
     if dtype == "e4m3":
-        mx8, mean8, _ = compare_attn(P, out, lse, segs, cu, idx, correction=correction, p8=True)
-        ref8 = P.attend_segments(segs, cu, idx, correction=correction, p8=True)[0]
-        ref = P.attend_segments(segs, cu, idx, correction=correction)[0]
-        inherent = float(np.abs(ref8 - ref).max())
-        _note(f"  vs Eq.15 oracle: max {mx8:.3e} mean {mean8:.3e}; Eq.15 itself vs exact {inherent:.3e}")
-        assert mx8 <= tmax and mean8 <= 1e-3
-        tmax = max(tmax, 1.25 * inherent)
-    assert mx <= tmax and mean <= tmean
+        mx, mean = check_e4m3(P, out, lse, segs, cu, idx, correction, tmax, tmean, note=_note)
+    else:
+        mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=correction)
+        _note(f"  attention corr={correction}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
+        assert mx <= tmax and mean <= tmean
     return mx, mean
 
 
