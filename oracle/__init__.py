@@ -96,6 +96,10 @@ def lib():
         L.fpo_attend_list.restype = None
         L.fpo_attend_list.argtypes = [P, dp, dp, C.c_int64, i64p, i32p, i32p, C.c_int, C.c_int,
                                       C.c_int, dp, dp]
+        L.fpo_block_mass_tile.restype = C.c_int64
+        L.fpo_block_mass_tile.argtypes = [P, dp, C.c_int, C.c_int, C.c_int64, dp, dp]
+        L.fpo_block_mass_list.restype = None
+        L.fpo_block_mass_list.argtypes = [P, dp, C.c_int64, i64p, C.c_int64, dp, dp]
         L.fpo_num_threads.restype = C.c_int
         L.fpo_num_threads.argtypes = []
     return _lib
@@ -312,6 +316,29 @@ class Problem:
         lse = np.zeros(self.rows, np.float64)
         lib().fpo_dense_tile(C.byref(self._s), b, h, I, _ptr(out, C.c_double), _ptr(lse, C.c_double))
         return out, lse
+
+    # -- exact block mass (selection-recall diagnostic) -------------------
+    def block_mass_tile(self, b, h, I):
+        """(mass, sur) over the tile's candidate blocks: the exact per-block attention
+        mass averaged over the tile's rows, and the mean surrogate for blocks J < beta."""
+        kb, _ = self.pool()
+        nc = self.candidates(b, I)
+        m = np.zeros(nc, np.float64)
+        su = np.zeros(nc, np.float64)
+        lib().fpo_block_mass_tile(C.byref(self._s), _ptr(kb, C.c_double), b, h, I,
+                                  _ptr(m, C.c_double), _ptr(su, C.c_double))
+        return m, su
+
+    def block_mass_segments(self, segs, max_nc=None):
+        """(mass, sur) of the listed segments, [n][max_nc] padded with -1 (OpenMP)."""
+        kb, _ = self.pool()
+        segs = np.ascontiguousarray(np.asarray(segs, np.int64))
+        mx = self.max_candidates() if max_nc is None else max_nc
+        m = np.zeros((len(segs), mx), np.float64)
+        su = np.zeros((len(segs), mx), np.float64)
+        lib().fpo_block_mass_list(C.byref(self._s), _ptr(kb, C.c_double), len(segs), _ptr(segs, C.c_int64),
+                                  mx, _ptr(m, C.c_double), _ptr(su, C.c_double))
+        return m, su
 
     # -- row mapping (definition of PackGQA, [V2] §3.3 Eq. 13) -----------
     def rows_of_segment(self, s):

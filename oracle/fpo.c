@@ -609,6 +609,75 @@ void fpo_attend_list(const fpo_problem* p, const double* kbar, const double* vba
   }
 }
 
+/* ------------------------------------------------------------------ */
+/* exact block attention mass (the selection-recall diagnostic)         */
+/* ------------------------------------------------------------------ */
+
+/* [V1] §3.1 "exact identification": every query of the tile is scored
+ * against every visible key, the per-query attention is summed within each
+ * block and then averaged over the tile's queries ("secondary averaging"):
+ *   mass_J = (1/n) sum_r sum_{i in B_J, i <= t_r} exp(sigma q_r.k_i - LSE_r),
+ * LSE_r the row's dense log-sum-exp, n the tile's valid rows, so that
+ * sum_J mass_J = 1.  For the blocks J < beta that every row sees whole, the
+ * mean surrogate the correction substitutes ([V2] Eq. 6; [V1] §3.1's
+ * Psi_pool = exp(q.k_bar) against Psi_sum, the AM-GM pair) is
+ *   sur_J = (1/n) sum_r |B_J| exp(sigma q_r.k_bar_J - LSE_r)  (0 for J >= beta),
+ * so sur_J <= mass_J.  Returns nc = beta1 + 1, the candidate count; both
+ * arrays hold nc entries. */
+int64_t fpo_block_mass_tile(const fpo_problem* p, const double* kbar, int b, int h, int64_t I,
+                            double* mass, double* sur) {
+  int g = group(p), d = p->d;
+  int64_t t0, t1, beta;
+  int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
+  int64_t nc = t1 / p->block + 1;
+  int64_t blk0 = fpo_block_offset(p, b);
+  double* qv = (double*)malloc(sizeof(double) * d);
+  double* kv = (double*)malloc(sizeof(double) * d);
+  double* a = (double*)malloc(sizeof(double) * (size_t)(t1 + 1));
+  for (int64_t J = 0; J < nc; ++J) mass[J] = sur[J] = 0.0;
+  for (int r = 0; r < nrows; ++r) {
+    int64_t pr = I * p->rows + r;
+    int64_t t = q_off(p, b) + pr / g;
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv);
+    double m = -INFINITY;
+    for (int64_t i = 0; i <= t; ++i) {
+      load_k(p, kv_start(p, b) + i, h, kv);
+      a[i] = p->scale * dot(qv, kv, d);
+      if (a[i] > m) m = a[i];
+    }
+    double den = 0.0;
+    for (int64_t i = 0; i <= t; ++i) den += exp(a[i] - m);
+    double lse = m + log(den);
+    for (int64_t i = 0; i <= t; ++i) mass[i / p->block] += exp(a[i] - lse);
+    for (int64_t J = 0; J < beta; ++J)
+      sur[J] += (double)p->block *
+                exp(p->scale * dot(qv, kbar_row(p, kbar, blk0, h, J), d) - lse);
+  }
+  for (int64_t J = 0; J < nc; ++J) {
+    mass[J] /= nrows;
+    sur[J] /= nrows;
+  }
+  free(qv);
+  free(kv);
+  free(a);
+  return nc;
+}
+
+/* mass / sur of a list of segments, [nlist][max_nc], padded with -1. */
+void fpo_block_mass_list(const fpo_problem* p, const double* kbar, int64_t nlist, const int64_t* segs,
+                         int64_t max_nc, double* mass, double* sur) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nlist; ++n) {
+    int32_t b, h;
+    int64_t I;
+    fpo_segment_coords(p, segs[n], &b, &h, &I);
+    double* mo = mass + (size_t)n * max_nc;
+    double* so = sur + (size_t)n * max_nc;
+    int64_t nc = fpo_block_mass_tile(p, kbar, b, h, I, mo, so);
+    for (int64_t J = nc; J < max_nc; ++J) mo[J] = so[J] = -1.0;
+  }
+}
+
 int fpo_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
