@@ -286,6 +286,75 @@ def chunked(args):
         torch.cuda.empty_cache()
 
 
+def segment_geometry(lengths, q_lengths, hq, hkv):
+    """(t0, t1) of every segment in (request, KV head, tile) order (host arithmetic)."""
+    g = hq // hkv
+    t0s, t1s = [], []
+    for L, Lq in zip(lengths, q_lengths):
+        nt = -(-g * Lq // 128)
+        r0 = 128 * np.arange(nt)
+        r1 = np.minimum(r0 + 128, g * Lq)
+        t0 = (L - Lq) + r0 // g
+        t1 = (L - Lq) + (r1 - 1) // g
+        for _ in range(hkv):
+            t0s.append(t0)
+            t1s.append(t1)
+    return np.concatenate(t0s), np.concatenate(t1s)
+
+
+def recall_stats(mass, sur, cu, idx, t0, t1, alpha, sink, win):
+    """What the selection keeps of the exact block mass ([V1] §3.1 exact identification)."""
+    nseg, mx = mass.shape
+    J = np.arange(mx)[None, :]
+    beta, nc = (t0 // 128)[:, None], (t1 // 128 + 1)[:, None]
+    cand = J < nc
+    sel = np.zeros((nseg, mx), bool)
+    seg_of = np.repeat(np.arange(nseg), np.diff(cu))
+    sel[seg_of, idx // 2] = True
+    m = np.where(cand, mass, 0.0).astype(np.float64)
+    su = np.where(cand, sur, 0.0).astype(np.float64)
+    corr = cand & ~sel & (J < beta)
+    forced = cand & ((J < sink) | ((J >= beta - win) & (J < beta)) | (J >= beta))
+    star = cand & (forced | (m >= alpha * m.max(1, keepdims=True)))
+    kept = (m * sel).sum(1)
+    return {
+        "mass_kept": float(kept.mean()), "mass_kept_min": float(kept.min()),
+        "missed_without_correction": float((1 - kept).mean()),
+        "missed_after_correction": float(((m - su) * corr).sum(1).mean()),
+        "am_gm_ratio_corrected": float((su * corr).sum() / max((m * corr).sum(), 1e-300)),
+        "exact_rule_block_recall": float((sel & star).sum() / star.sum()),
+        "exact_rule_density": float(star.sum() / cand.sum()), "density": float(sel.sum() / cand.sum()),
+    }
+
+
+def recall(args):
+    """Selection recall against the exact block mass for the 32K and 128K layers:
+    one JSON line per workload (fp_block_mass timed on the GPU)."""
+    from block_sparse_long_mean_amd import fp
+
+    for w in (configs.L32K, configs.L128K):
+        batch, _ = w.make()
+        case = Case(batch, None, w.alpha, w.sink_blocks, w.window_blocks)
+        case.select()
+        case.dense()
+        cu, idx = case.csr()
+        lse = case.lse.clone()
+        n, mx = case.bufs.sizes.n_segments, case.bufs.sizes.max_blocks
+        mass = torch.empty((n, mx), dtype=torch.float32, device="cuda")
+        sur = torch.empty((n, mx), dtype=torch.float32, device="cuda")
+        ms = float(np.median(time_calls(lambda: fp.block_mass(case.B, case.q, case.k, lse, case.bufs, mass, sur),
+                                        3, 1)))
+        t0, t1 = segment_geometry(batch.lengths, batch.q_lengths, batch.hq, batch.hkv)
+        st = recall_stats(mass.cpu().numpy(), sur.cpu().numpy(), cu, idx, t0, t1, w.alpha, w.sink_blocks,
+                          w.window_blocks)
+        qk = dense_flops(batch.lengths, batch.hq, batch.q_lengths) / 2  # Q K^T of every visible pair
+        print(json.dumps({"recall": w.name, "alpha": w.alpha, "block_mass_ms": ms,
+                          "block_mass_tflops": qk / (ms / 1e3) / 1e12,
+                          "block_mass_mfma_frac": qk / (ms / 1e3) / 1e12 / PEAK[batch.dtype], **st}), flush=True)
+        del case, mass, sur
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +372,8 @@ def main():
     ap.add_argument("--chunked", action="store_true",
                     help="the 128K prompt in 8K and 16K chunks (index rebuilt per chunk) against one pass: "
                          "one JSON line per chunk size")
+    ap.add_argument("--recall", action="store_true",
+                    help="selection recall against the exact block mass (32K and 128K layers): one JSON line each")
     args = ap.parse_args()
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -320,6 +391,9 @@ def main():
         return
     if args.chunked:
         chunked(args)
+        return
+    if args.recall:
+        recall(args)
         return
 
     w = configs.ALL[args.config]

@@ -361,6 +361,21 @@ fp_status fp_dense_attn(const fp_problem* prob, const void* q, const void* k, co
   return run_attn(prob, q, k, v, nullptr, nullptr, nullptr, 1, 0, out, lse, ws, ws_bytes, stream);
 }
 
+fp_status fp_block_mass(const fp_problem* prob, const void* q, const void* k, const float* lse,
+                        const void* means, float* mass, float* surrogate, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Prepared pr;
+  fp_status s = prepare(prob, ws, ws_bytes, &pr);
+  if (s != FP_OK) return s;
+  if (!q || !k || !lse || !mass) return fail(FP_ERR_INVALID_ARG, "q, k, lse and mass are required");
+  if (surrogate && !means) return fail(FP_ERR_INVALID_ARG, "the surrogate needs the pooled means");
+  if (pr.hg.total == 0) return FP_OK;
+  hipStream_t st = (hipStream_t)stream;
+  FP_LAUNCH(launch_meta(pr.g, st));
+  FP_LAUNCH(launch_block_mass(pr.g, pr.ml, q, k, lse, (const char*)means, mass, surrogate, st));
+  return FP_OK;
+}
+
 fp_status fp_read_device_error(void* ws, void* stream, int32_t* flag) {
   if (!ws || !flag) return fail(FP_ERR_INVALID_ARG, "ws and flag are required");
   hipStream_t st = (hipStream_t)stream;

@@ -93,6 +93,8 @@ hipError_t launch_attn(const Geo& g, const WsLayout& wl, char* ws, const MeansLa
                        const void* q, const void* k, const void* v, const int32_t* cu,
                        const int32_t* idx, const char* means, int dense, int correction,
                        void* out, float* lse, int grid, hipStream_t st);
+hipError_t launch_block_mass(const Geo& g, const MeansLayout& ml, const void* q, const void* k,
+                             const float* lse, const char* means, float* mass, float* sur, hipStream_t st);
 hipError_t launch_combine(const Geo& g, const WsLayout& wl, char* ws, void* out, float* lse,
                           hipStream_t st);
 

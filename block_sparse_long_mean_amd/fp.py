@@ -64,6 +64,8 @@ _lib.fp_sparse_attn.argtypes = [_P, _SP, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int32
                                 C.c_size_t, _vp]
 _lib.fp_dense_attn.restype = C.c_int
 _lib.fp_dense_attn.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+_lib.fp_block_mass.restype = C.c_int
+_lib.fp_block_mass.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
 _lib.fp_read_device_error.restype = C.c_int
 _lib.fp_read_device_error.argtypes = [_vp, _vp, C.POINTER(C.c_int32)]
 _lib.fp_block_base.restype = C.c_int64
@@ -190,6 +192,13 @@ def sparse_attn(batch: Batch, params: SelectParams, q, k, v, bufs: Buffers, out,
 def dense_attn(batch: Batch, q, k, v, bufs: Buffers, out, lse=None):
     _check(_lib.fp_dense_attn(batch.ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(bufs.ws),
                               bufs.ws.numel(), _stream()))
+
+
+def block_mass(batch: Batch, q, k, lse, bufs: Buffers, mass, surrogate=None):
+    """Exact per-block attention mass [n_segments, max_blocks] (and the mean surrogate);
+    ``lse`` from :func:`dense_attn`, ``bufs.means`` from :func:`select` or :func:`pool`."""
+    _check(_lib.fp_block_mass(batch.ptr, _ptr(q), _ptr(k), _ptr(lse), _ptr(bufs.means), _ptr(mass),
+                              _ptr(surrogate), _ptr(bufs.ws), bufs.ws.numel(), _stream()))
 
 
 def read_device_error(bufs: Buffers) -> int:

@@ -16,6 +16,10 @@
  *                   listed tiles, plus one mean-correction term per pruned
  *                   block that every row of the tile can see.
  *   fp_dense_attn   dense causal attention on the same kernel (the baseline).
+ * and one diagnostic:
+ *   fp_block_mass   exact per-block attention mass of every query tile, and
+ *                   the mean surrogate of the blocks the correction replaces
+ *                   (how much attention the selection keeps).
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
@@ -139,7 +143,8 @@ fp_status fp_pool(const fp_problem* prob, const void* k, const void* v, void* me
  * < beta, J == beta), and CSR expansion of each kept block J into tiles 2J and
  * 2J+1 (a tile starting after the tile's last query position is dropped).
  * energies (optional, may be NULL): [n_segments][max_blocks] floats receive
- * E_J / max E for J <= beta and -1 beyond.  idx_capacity is the int32 size of
+ * E_J / max E for the candidate blocks J <= beta1 (the block of the segment's
+ * last position) and -1 beyond.  idx_capacity is the int32 size of
  * idx and must be >= fp_sizes.idx_capacity. */
 fp_status fp_select(const fp_problem* prob, const fp_select_params* params, const void* q,
                     const void* k, const void* v, int32_t* cu, int32_t* idx,
@@ -163,6 +168,27 @@ fp_status fp_sparse_attn(const fp_problem* prob, const fp_select_params* params,
  * pipeline).  lse is optional. */
 fp_status fp_dense_attn(const fp_problem* prob, const void* q, const void* k, const void* v,
                         void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Exact block attention mass, the selection-recall diagnostic ("FlashPrefill:
+ * Instantaneous Pattern Discovery and Thresholding for Ultra-Fast Long-Context
+ * Prefilling", §3.1: exact identification scores every query against every
+ * key and averages the per-block attention over the tile's queries; its
+ * AM-GM argument pairs the pooled surrogate with the true block sum).  For
+ * each segment s and candidate block J <= beta1 (n = the segment's valid rows,
+ * t_r a row's position, LSE_r its dense log-sum-exp):
+ *   mass[s][J]      = (1/n) sum_r sum_{i in block J, i <= t_r} exp(sigma q_r.k_i - LSE_r)
+ *   surrogate[s][J] = (1/n) sum_r 128 exp(sigma q_r.kbar_J - LSE_r)  for J < beta,
+ *                     0 for beta <= J <= beta1
+ * and -1 for J > beta1.  Both are [n_segments][max_blocks] floats; a
+ * segment's masses sum to 1.  lse: [total_q][num_heads_q] natural-log dense
+ * LSE of the same rows (required): fp_dense_attn's for fp32 and bf16 inputs;
+ * for E4M3 inputs that of the descaled values (fp_dense_attn on their fp32
+ * decoding), since the E4M3 path's LSE carries Eq. 15's rounding.  surrogate may be NULL; when
+ * given, means must hold fp_pool's (or fp_select's) output for this problem.
+ * Costs about half a dense attention call (Q K^T of every visible pair). */
+fp_status fp_block_mass(const fp_problem* prob, const void* q, const void* k, const float* lse,
+                        const void* means, float* mass, float* surrogate, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Synchronises `stream`, then reads and clears the device error flag of the
  * workspace.  *flag (host) receives the flag bits (0 = no error; bit 0: page

@@ -153,6 +153,14 @@ def test_calls_fail_before_launch_on_small_buffers():
     r = lib.fp_dense_attn(C.byref(p), dummy, dummy, dummy, dummy, None, None, s.workspace_bytes, None)
     assert r == -1
     assert lib.fp_status_string(-3) == b"workspace too small"
+    # block mass: lse and mass are required; the surrogate needs the means
+    r = lib.fp_block_mass(C.byref(p), dummy, dummy, None, dummy, dummy, None, dummy, s.workspace_bytes, None)
+    assert r == -1
+    r = lib.fp_block_mass(C.byref(p), dummy, dummy, dummy, None, dummy, dummy, dummy, s.workspace_bytes, None)
+    assert r == -1
+    r = lib.fp_block_mass(C.byref(p), dummy, dummy, dummy, None, dummy, None, dummy, s.workspace_bytes - 1,
+                          None)
+    assert r == -3
 
 
 def test_chunked_problem_geometry_and_checks():

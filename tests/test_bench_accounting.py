@@ -40,3 +40,39 @@ def test_csr_work_matches_brute_force(lengths, qlens, correction):
             assert alg == bench.dense_flops(b.lengths, b.hq, b.q_lengths)
             assert dens == 1.0
         assert execd >= alg
+
+
+def test_segment_geometry_and_recall_stats():
+    """bench.py's segment positions match the oracle's tiles; its recall figures
+    match per-segment loops over the oracle's masses and index."""
+    b = synth.make_batch([1500, 700], 8, 2, 128, seed=12, dtype="f32", clusters=True, diag_bias=True,
+                         q_lengths=[411, 700])
+    P = oracle_problem(b)
+    nseg = P.num_segments()
+    t0, t1 = bench.segment_geometry(b.lengths, b.q_lengths, b.hq, b.hkv)
+    for s in range(nseg):
+        bb, _, I = P.segment_coords(s)
+        _, o0, o1, _ = P.tile_info(bb, I)
+        assert (t0[s], t1[s]) == (o0, o1)
+    cu, idx = P.select_all(0.3, 1, 2)
+    m, su = P.block_mass_segments(range(nseg))
+    st = bench.recall_stats(m, su, cu, idx, t0, t1, 0.3, 1, 2)
+    kept, miss_c, corr_m, corr_s, rec_n, rec_d = [], [], 0.0, 0.0, 0, 0
+    for s in range(nseg):
+        bb, _, I = P.segment_coords(s)
+        beta, nc = P.tile_info(bb, I)[3], P.candidates(bb, I)
+        sel = set((idx[cu[s]:cu[s + 1]] // 2).tolist())
+        kept.append(sum(m[s, J] for J in sel))
+        cj = [J for J in range(beta) if J not in sel]
+        miss_c.append(sum(m[s, J] - su[s, J] for J in cj))
+        corr_m += sum(m[s, J] for J in cj)
+        corr_s += sum(su[s, J] for J in cj)
+        mx = m[s, :nc].max()
+        star = {J for J in range(nc) if J < 1 or beta - 2 <= J < beta or J >= beta or m[s, J] >= 0.3 * mx}
+        rec_n += len(star & sel)
+        rec_d += len(star)
+    assert abs(st["mass_kept"] - np.mean(kept)) < 1e-12
+    assert abs(st["missed_after_correction"] - np.mean(miss_c)) < 1e-12
+    assert abs(st["am_gm_ratio_corrected"] - corr_s / corr_m) < 1e-12
+    assert st["exact_rule_block_recall"] == rec_n / rec_d
+    assert 0 <= st["missed_after_correction"] <= st["missed_without_correction"]
