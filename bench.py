@@ -130,8 +130,9 @@ def time_calls(fn, steps, warmup):
 
 
 class Case:
-    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4, dev=None):
-        """``dev``: (q, k, v) already on the device (views are fine), else uploaded."""
+    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4, dev=None, v_cols=False):
+        """``dev``: (q, k, v) already on the device (views are fine), else uploaded.
+        ``v_cols``: E4M3 V stored transposed (contiguous only)."""
         from block_sparse_long_mean_amd import fp
 
         self.fp = fp
@@ -143,9 +144,10 @@ class Case:
                                    descale=batch.descale if batch.dtype == "e4m3" else None)
         elif paged is None:
             self.q = batch.q.cuda()
-            self.k, self.v = batch.k.cuda(), batch.v.cuda()
+            self.k = batch.k.cuda()
+            self.v = (synth.v_columns(batch) if v_cols else batch.v).cuda()
             self.B = fp.make_batch(batch.cu, batch.hq, batch.hkv, tdt, cu_seqlens_kv=batch.cu_kv,
-                                   descale=batch.descale if batch.dtype == "e4m3" else None)
+                                   descale=batch.descale if batch.dtype == "e4m3" else None, v_cols=v_cols)
         else:
             self.q = batch.q.cuda()
             self.k, self.v = paged.k_pool.cuda(), paged.v_pool.cuda()
@@ -443,6 +445,16 @@ def main():
                     variants["fp8_dense_ms"] = dd
                     variants["fp8_speedup_vs_dense"] = dd / m["step_ms"]
                 del c8
+            # V stored transposed (the column-major FP8 layout, consumed without a transpose)
+            c8 = Case(b8, None, 0.1, w.sink_blocks, w.window_blocks, v_cols=True)
+            m = measure(c8, 5, 2, correction=True)
+            variants["fp8_vcols_alpha0.1"] = {
+                "select_ms": m["select_ms"], "attn_ms": m["attn_ms"], "step_ms": m["step_ms"],
+                "density": m["density"], "eff_tflops": F / (m["step_ms"] / 1e3) / 1e12,
+                "attn_alg_tflops": m["attn_alg_flop"] / (m["attn_ms"] / 1e3) / 1e12}
+            dd = float(np.median(time_calls(c8.dense, 3, 1)))
+            variants["fp8_vcols_dense_ms"] = dd
+            del c8
         extra["variants"] = variants
     res = {
         "metric": METRIC,

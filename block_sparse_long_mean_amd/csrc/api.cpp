@@ -56,6 +56,10 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
   if (p->dtype != FP_F32 && p->dtype != FP_BF16 && p->dtype != FP_E4M3)
     return fail(FP_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
   if (p->dtype == FP_E4M3 && !p->descale) return fail(FP_ERR_INVALID_ARG, "E4M3 inputs need descale[3]");
+  if (p->v_layout != FP_V_ROWS && p->v_layout != FP_V_COLS)
+    return fail(FP_ERR_INVALID_ARG, "unknown v_layout %d", p->v_layout);
+  if (p->v_layout == FP_V_COLS && p->dtype != FP_E4M3)
+    return fail(FP_ERR_UNSUPPORTED, "column-major V is an E4M3 layout");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale >= 0.f))
     return fail(FP_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
   const int32_t* cu = p->cu_seqlens_q_host;
@@ -111,6 +115,22 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
       return fail(FP_ERR_INVALID_ARG, "max_pages_per_req * page_size (%lld) < longest request (%lld)",
                   (long long)p->max_pages_per_req * p->page_size, (long long)max_len);
     if (p->num_pool_slots < 1) return fail(FP_ERR_INVALID_ARG, "num_pool_slots must be >= 1");
+  }
+  if (p->v_layout == FP_V_COLS) {
+    if (p->page_table && (p->page_size % kTile || p->num_pool_slots % p->page_size))
+      return fail(FP_ERR_UNSUPPORTED, "column-major paged V needs a page size that is a multiple of %d and "
+                  "num_pool_slots a multiple of it", kTile);
+    // a head's transposed values are addressed through one 32-bit buffer range
+    if (!p->page_table && (uint64_t)kD * (uint64_t)hg->total_kv >= 0xfffff000ull)
+      return fail(FP_ERR_UNSUPPORTED, "column-major V of %lld rows exceeds the 4 GiB addressing range",
+                  (long long)hg->total_kv);
+    // 16-byte pieces of a transposed row are loaded whole: rows start 16-aligned
+    if (!p->page_table) {
+      for (int b = 0; b <= p->num_reqs; ++b)
+        if (ckv[b] % 16)
+          return fail(FP_ERR_UNSUPPORTED, "contiguous column-major V needs every K/V offset to be a "
+                      "multiple of 16 (offset %d of request %d)", ckv[b], b);
+    }
   }
   return FP_OK;
 }
@@ -205,6 +225,8 @@ Geo make_geo(const fp_problem* p, const HostGeo& hg, char* ws, const WsLayout& w
   g.log2g = hg.log2g;
   g.dtype = p->dtype;
   g.descale = p->descale;
+  g.vcols = p->v_layout == FP_V_COLS ? 1 : 0;
+  g.vrow = p->page_table ? p->page_size : hg.total_kv;
   g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.f / std::sqrt((float)p->head_dim);
   g.max_nj = hg.max_nj;
   g.words = hg.words;

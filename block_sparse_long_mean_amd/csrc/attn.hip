@@ -271,7 +271,7 @@ __device__ __forceinline__ uint32_t paged_off(const Geo& g, const SegCoord& c, i
 constexpr uint32_t kNaN32 = 0x7fc00000u;
 constexpr uint32_t kNaNbf16x2 = 0x7fc07fc0u;
 
-template <int DT, bool DENSE, int AM>
+template <int DT, bool DENSE, int AM, bool VC = false>
 __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     Geo g, WsLayout wl, char* __restrict__ ws, MeansLayout ml, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ cu,
@@ -407,6 +407,10 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const uint64_t mbase = ((uint64_t)g.blk_base[c.b] * g.hkv + c.h) * kD * EB;
     const char* kmbase = means + ml.kop + mbase;
     const char* vmbase = means + ml.vop + mbase;
+    // transposed V (e4m3): this head's dim rows, and the transposed correction
+    // operands ([chunk][head][dim][64 blocks]) of the request's first chunk
+    const char* vtbase = (const char*)v + (AM == kContig ? (uint64_t)c.h * kD * g.vrow + c.kv0 : 0);
+    const char* vtmbase = means + ml.vop + (uint64_t)((g.blk_base[c.b] >> 6) * g.hkv + c.h) * kD * kChunk;
     const uint64_t mbytes = (uint64_t)(((t.beta + kChunk - 1) / kChunk) * kChunk) * rowstride;
 
     if (NC > 0) {
@@ -806,6 +810,32 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         dv[qq] = (uint32_t)r * rowstride + (uint32_t)((cl ^ swz_v<DT>(r)) * 16);
       }
     }
+    // transposed V (VC): instruction qq of wave w fills dim rows 16 (2w + qq) ..
+    // +15, four 16-byte pieces (keys 16 cs .. +15) per 64-byte row; the piece in
+    // slot cl of row r holds logical piece cl ^ ((r >> 2) & 3), so that the
+    // operand reads of 16 consecutive rows fall on distinct banks
+    uint32_t dvt[2], dvm[2];
+    int vt_cs[2];
+    if constexpr (VC) {
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const int r = 16 * (2 * wave + qq) + (lane >> 2);
+        const int cs = (lane & 3) ^ ((r >> 2) & 3);
+        vt_cs[qq] = cs;
+        dvt[qq] = (uint32_t)(r * g.vrow + 16 * cs);
+        dvm[qq] = (uint32_t)(r * kChunk + 16 * cs);
+      }
+    }
+    // DMA of a transposed V tile (keys j0 .. j0 + 63 of every dim row; pieces
+    // starting at or past the request's end read as zero)
+    auto dma_vt = [&](int buf, __amdgpu_buffer_rsrc_t rv, int j0, bool means_tile) {
+      char* vs = smem + buf * C::STAGE + C::KBYTES;
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) {
+        const uint32_t o = means_tile ? dvm[qq] : (j0 + 16 * vt_cs[qq] < c.L ? dvt[qq] : 0xfffffff0u);
+        dma16(rv, vs + 16 * (2 * wave + qq) * 64, o);
+      }
+    };
     Vec8<DT> kst[C::DMA ? 1 : 4], vst[C::DMA ? 1 : 4];
 
     // DMA of one 64-row K and V tile (rows past the range read as zero)
@@ -816,7 +846,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       for (int qq = 0; qq < C::NDMA; ++qq) {
         const int r0 = 16 * wave + C::RPI * qq;
         dma16(rk, ks + r0 * C::ROWB, dk[qq]);
-        dma16(rv, vs + r0 * C::ROWB, dv[qq]);
+        if constexpr (!VC) dma16(rv, vs + r0 * C::ROWB, dv[qq]);
       }
     };
     // paged, any page size: one page-table lookup per row; rows past the request
@@ -862,6 +892,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           const uint64_t o = (uint64_t)j0 * rowstride;
           const uint64_t left = kvbytes > o ? kvbytes - o : 0;
           const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
+          if constexpr (VC) {
+            // this head's dim rows from key j0 on, up to the end of its last row
+            const uint64_t vleft = (uint64_t)kD * g.vrow - (uint64_t)(c.kv0 + j0);
+            dma_vt(buf, make_rsrc(vtbase + j0, vleft), j0, false);
+          }
           if constexpr (C::DMA) {
             dma_tile(buf, rk, rv);
           } else {
@@ -884,6 +919,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           const uint64_t tail = (uint64_t)max(0, c.L - 1 - j0) * rowstride + C::ROWB;
           const uint64_t left = min(kvbytes > o ? kvbytes - o : (uint64_t)0, tail);
           const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + o, left), rv = make_rsrc(vbase + o, left);
+          if constexpr (VC) {
+            // page [head][dim][p]: this head's dim rows of the page, from key j0 on
+            const int64_t pg0 = slot0 / g.page_size, in_pg = slot0 - pg0 * g.page_size;
+            const char* vb = (const char*)v + ((uint64_t)(pg0 * g.hkv + c.h) * kD) * g.page_size + in_pg;
+            dma_vt(buf, make_rsrc(vb, (uint64_t)kD * g.page_size - in_pg), j0, false);
+          }
           if constexpr (C::DMA) {
             dma_tile(buf, rk, rv);
           } else {
@@ -912,6 +953,10 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
         const uint64_t left = mbytes > o ? mbytes - o : 0;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kmbase + o, left), rv = make_rsrc(vmbase + o, left);
+        if constexpr (VC) {
+          const uint64_t mo = (uint64_t)(it - T) * g.hkv * kD * kChunk;
+          dma_vt(buf, make_rsrc(vtmbase + mo, (uint64_t)kD * kChunk), 0, true);
+        }
         if constexpr (C::DMA) {
           dma_tile(buf, rk, rv);
         } else {
@@ -964,7 +1009,17 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     };
     // MFMA A operand m1 of output tile nt (V^T) from stage buffer
     auto v_op = [&](const char* vs, int nt, int m1) -> Op {
-      if constexpr (DT == kE4M3) {
+      if constexpr (VC) {
+        // dim row nt*32 + col, keys 32 half .. +31 (logical pieces 2 half, 2 half + 1)
+        const int d = nt * 32 + col, sw = (d >> 2) & 3;
+        const char* rp = vs + d * 64;
+        const uint4 a = *(const uint4*)(rp + (((2 * half) ^ sw) << 4));
+        const uint4 b = *(const uint4*)(rp + (((2 * half + 1) ^ sw) << 4));
+        i32x8 r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        return r;
+      } else if constexpr (DT == kE4M3) {
         // 32 keys of column nt*32 + lane%32 in the register order of P: read t
         // (0..3) gives keys 16 t + 8 (i/4) + 4 half + i%4, i = 0..7
         const int k16 = lane & 15;
@@ -1098,6 +1153,22 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             psum += (back[0] + back[1]) + (back[2] + back[3]);
             b[w] = (int)word;
           }
+          if constexpr (VC) {
+            // word w of lane half h holds keys 4 gi .. 4 gi + 3, gi = 8 (w / 4) +
+            // 2 (w % 4) + h; exchange halves so that half h holds keys 32 h .. 32 h
+            // + 31 in order, matching the transposed V rows.  One lane-half swap
+            // per pair (w, w + 4): the first result is [own w | half 0's w + 4],
+            // the second [half 1's w | own w + 4], i.e. words 2j and 2j + 1 of
+            // either half.
+            i32x8 nb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)b[j], (uint32_t)b[4 + j], false, false);
+              nb[2 * j] = (int)r[0];
+              nb[2 * j + 1] = (int)r[1];
+            }
+            b = nb;
+          }
           pf[0] = b;
           l_i += psum;
         } else {
@@ -1110,10 +1181,35 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
           l_i += psum;
         }
+        if constexpr (VC && KIND == 0) {
+          // the tile holding the request's last key: bytes of keys past the end
+          // (another request's values, or unused page slots) are cleared, so
+          // that a zero weight never meets a NaN
+          const int nvalid = c.L - cur_tile * kTile - 32 * half;
+          if (__any(nvalid < 32)) {
+            uint32_t bm[8];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
+            for (int w = 0; w < 8; ++w) {
+              const int nb = min(4, max(0, nvalid - 4 * w));
+              bm[w] = nb == 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+            }
 #pragma unroll
-          for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
+            for (int nt = 0; nt < 4; ++nt) {
+              Op a = v_op(vt, nt, 0);
+#pragma unroll
+              for (int w = 0; w < 8; ++w) a[w] &= bm[w];
+              oacc[nt] = mma<DT>(a, pf[0], oacc[nt]);
+            }
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) oacc[nt] = mma<DT>(v_op(vt, nt, 0), pf[0], oacc[nt]);
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+            for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
+          }
         }
       } else {
         // Two halves of 32 keys (logit tile jt), each an online-softmax update
@@ -1335,20 +1431,20 @@ __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const 
 
 int attn_wgs_per_cu(int dtype) { return dtype == kF32 ? Cfg<kF32>::WGS : Cfg<kBF16>::WGS; }
 
-template <int DT, bool DENSE, int AM>
+template <int DT, bool DENSE, int AM, bool VC = false>
 static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, const MeansLayout& ml,
                                 const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* idx, const char* means, int correction, void* out,
                                 float* lse, int grid, hipStream_t st) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, AM>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, AM, VC>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<DT>::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  attn_kernel<DT, DENSE, AM><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
-                                                                  correction, out, lse);
+  attn_kernel<DT, DENSE, AM, VC><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
+                                                                      correction, out, lse);
   return hipGetLastError();
 }
 
@@ -1358,6 +1454,15 @@ static hipError_t launch_attn_dt(const Geo& g, const WsLayout& wl, char* ws, con
                                  const int32_t* idx, const char* means, int dense, int correction,
                                  void* out, float* lse, int grid, hipStream_t st) {
   const int am = !g.page_table ? kContig : (g.page_size % kTile == 0 ? kPagedTile : kPagedAny);
+  if constexpr (DT == kE4M3) {
+    if (g.vcols) {  // transposed V: contiguous or 64-multiple pages (checked on the host)
+#define FP_VC(DENSE, AMV) \
+  launch_attn_t<DT, DENSE, AMV, true>(g, wl, ws, ml, q, k, v, cu, idx, means, DENSE ? 0 : correction, out, lse, grid, st)
+      if (dense) return am == kContig ? FP_VC(true, kContig) : FP_VC(true, kPagedTile);
+      return am == kContig ? FP_VC(false, kContig) : FP_VC(false, kPagedTile);
+#undef FP_VC
+    }
+  }
 #define FP_AM(DENSE, AMV) \
   launch_attn_t<DT, DENSE, AMV>(g, wl, ws, ml, q, k, v, cu, idx, means, DENSE ? 0 : correction, out, lse, grid, st)
   if (dense) return am == kContig ? FP_AM(true, kContig) : am == kPagedTile ? FP_AM(true, kPagedTile) : FP_AM(true, kPagedAny);

@@ -47,6 +47,8 @@ struct Geo {
   int32_t nreq, hq, hkv, g, log2g;
   int32_t dtype;
   const float* descale;       // [3] for E4M3
+  int32_t vcols;              // V stored transposed (E4M3): a head's values are rows of vrow bytes
+  int64_t vrow;               // bytes from one dim's row of V^T to the next (total_kv, or page size)
   float scale;                // sigma
   int32_t max_nj;             // largest candidate-block count of a segment
   int32_t words;              // selection bitmask words per segment

@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
   const float ck = DT == kE4M3 ? g.descale[1] : 1.f;
   const float cv = DT == kE4M3 ? g.descale[2] : 1.f;
 
+  const bool vcols = DT == kE4M3 && g.vcols;  // V stored transposed: pooled below
   const int chunk = tid & 15, tg = tid >> 4;
   float sk[8], sv[8];
 #pragma unroll
@@ -123,11 +124,11 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
     int64_t el = (row * g.hkv + h) * kD + chunk * 8;
     float a[8], b[8];
     load8<DT>(k, el, ck, a);
-    load8<DT>(v, el, cv, b);
+    if (!vcols) load8<DT>(v, el, cv, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       sk[e] += a[e];
-      sv[e] += b[e];
+      if (!vcols) sv[e] += b[e];
     }
   }
 #pragma unroll
@@ -136,6 +137,45 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
     red[1][tg][chunk * 8 + e] = sv[e];
   }
   __syncthreads();
+  if (vcols) {
+    // transposed V: thread (dim d, half hf) sums tokens 64 hf .. 64 hf + 63 of
+    // the block, contiguous in dim d's row (16-byte pieces; the last piece is
+    // masked past the block's n tokens); its partial replaces row hf of red[1]
+    const int d = tid & 127, hf = tid >> 7;
+    const int j0 = J * kBlock + 64 * hf;
+    const int cnt = max(0, min(64, n - 64 * hf));
+    float s = 0.f;
+    if (cnt > 0) {
+      int64_t rowb;  // byte offset of token j0 of dim d
+      if (!g.page_table) {
+        rowb = ((int64_t)h * kD + d) * g.vrow + c.kv0 + j0;
+      } else {
+        const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + j0 / g.page_size];
+        if (page < 0 || (page + 1) * g.page_size > g.num_slots) {
+          atomicOr(&g.hdr->err, kErrPage);
+          rowb = -1;
+        } else {
+          rowb = ((page * g.hkv + h) * kD + d) * g.page_size + j0 % g.page_size;
+        }
+      }
+      if (rowb >= 0) {
+        const uint8_t* p = (const uint8_t*)v + rowb;
+        for (int c16 = 0; 16 * c16 < cnt; ++c16) {
+          const uint4 w = *(const uint4*)(p + 16 * c16);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 f = e4m3x4_to_f32(ww[q4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * c16 + 4 * q4 + e < cnt) s += f[e];
+          }
+        }
+      }
+    }
+    red[1][hf][d] = s * cv;
+    __syncthreads();
+  }
   const int which = tid >> 7, d = tid & 127;
   float s = 0.f;
 #pragma unroll
@@ -151,7 +191,9 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
   } else if constexpr (DT == kF32) {
     ((float*)op)[row_el] = mean;
   } else {
-    ((uint8_t*)op)[row_el] = (uint8_t)f32x2_to_e4m3x2(mean / (which ? cv : ck), 0.f);
+    // transposed V: the correction operands of a 64-block chunk are [dim][block]
+    const int64_t el = which && vcols ? (((gb >> 6) * g.hkv + h) * kD + d) * kChunk + (gb & 63) : row_el;
+    ((uint8_t*)op)[el] = (uint8_t)f32x2_to_e4m3x2(mean / (which ? cv : ck), 0.f);
   }
   if (which == 0) {
     // kbar = hi + lo in bf16, stored in MFMA B-operand order:

@@ -37,6 +37,7 @@ class Problem(C.Structure):
         ("num_pool_slots", C.c_int64), ("dtype", C.c_int32), ("descale", C.c_void_p),
         ("softmax_scale", C.c_float),
         ("cu_seqlens_kv", C.c_void_p), ("cu_seqlens_kv_host", C.c_void_p),
+        ("v_layout", C.c_int32),
     ]
 
 
@@ -120,10 +121,11 @@ class Batch:
 
 def make_batch(cu_seqlens, num_heads_q, num_heads_kv, dtype, device="cuda", head_dim=128,
                page_table=None, page_size=0, num_pool_slots=0, descale=None, softmax_scale=0.0,
-               cu_seqlens_kv=None) -> Batch:
+               cu_seqlens_kv=None, v_cols=False) -> Batch:
     """Build the C problem struct.  ``cu_seqlens`` (query rows) and ``cu_seqlens_kv`` (K/V
     lengths; None = the same) are host sequences; ``dtype`` a torch dtype (float32, bfloat16,
-    or uint8 for E4M3 codes); ``page_table`` a host int array or None."""
+    or uint8 for E4M3 codes); ``page_table`` a host int array or None; ``v_cols``: V is stored
+    transposed (E4M3 only, see fp.h)."""
     cu_host = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     cu_dev = torch.from_numpy(cu_host.copy()).to(device)
     kv_host = kv_dev = None
@@ -142,7 +144,7 @@ def make_batch(cu_seqlens, num_heads_q, num_heads_kv, dtype, device="cuda", head
     prob = Problem(len(cu_host) - 1, num_heads_q, num_heads_kv, head_dim, cu_dev.data_ptr(),
                    cu_host.ctypes.data, _ptr(pt), page_size if pt is not None else 0, max_pages,
                    num_pool_slots if pt is not None else 0, _DT[dtype], _ptr(ds), softmax_scale,
-                   _ptr(kv_dev), None if kv_host is None else kv_host.ctypes.data)
+                   _ptr(kv_dev), None if kv_host is None else kv_host.ctypes.data, 1 if v_cols else 0)
     return Batch(prob, cu_dev, cu_host, pt, ds, kv_dev, kv_host)
 
 

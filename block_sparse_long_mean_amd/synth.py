@@ -192,22 +192,29 @@ def varlen_lengths(n, lo, hi, seed):
     return [int(math.floor(math.exp(t))) for t in x]
 
 
+def v_columns(batch: Batch) -> torch.Tensor:
+    """V stored transposed, [Hkv][d][total_kv]: each head's value vectors as
+    columns (the column-major FP8 V layout; layout only)."""
+    return batch.v.permute(1, 2, 0).contiguous()
+
+
 @dataclass
 class Paged:
     """K/V scattered into a pool of pages through a page table ([V2] §3.3 Eq. 22)."""
 
     k_pool: torch.Tensor          # [num_slots, hkv, d]
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor          # [num_slots, hkv, d], or [num_pages, hkv, d, page_size] (v_cols)
     page_table: np.ndarray        # [num_reqs, max_pages] int32 (-1 = unused)
     page_size: int
     num_slots: int
 
 
-def page_kv(batch: Batch, page_size, seed, spare=0.05, poison=True) -> Paged:
+def page_kv(batch: Batch, page_size, seed, spare=0.05, poison=True, v_cols=False) -> Paged:
     """Scatter K/V into a page pool with a random permutation of page ids.
 
     The pool holds sum ceil(L_b/p) pages plus ``spare`` extra, and every slot
     no request owns is filled with NaN so a stray read shows in the output.
+    ``v_cols``: each V page is stored transposed, [Hkv][d][page_size].
     """
     need = [(L + page_size - 1) // page_size for L in batch.lengths]
     npages = int(sum(need) + math.ceil(spare * sum(need)))
@@ -222,7 +229,7 @@ def page_kv(batch: Batch, page_size, seed, spare=0.05, poison=True) -> Paged:
     slots = npages * page_size
     shape = (slots, batch.hkv, batch.d)
     kp = torch.empty(shape, dtype=batch.k.dtype)
-    vp = torch.empty(shape, dtype=batch.v.dtype)
+    vp = torch.empty((npages, batch.hkv, batch.d, page_size) if v_cols else shape, dtype=batch.v.dtype)
     if poison:
         if batch.k.dtype == torch.uint8:
             kp.fill_(0x7F)  # E4M3 NaN code
@@ -237,5 +244,8 @@ def page_kv(batch: Batch, page_size, seed, spare=0.05, poison=True) -> Paged:
             hi = min(L, lo + page_size)
             s0 = int(pt[b, j]) * page_size
             kp[s0:s0 + hi - lo] = batch.k[base + lo:base + hi]
-            vp[s0:s0 + hi - lo] = batch.v[base + lo:base + hi]
+            if v_cols:
+                vp[int(pt[b, j]), :, :, :hi - lo] = batch.v[base + lo:base + hi].permute(1, 2, 0)
+            else:
+                vp[s0:s0 + hi - lo] = batch.v[base + lo:base + hi]
     return Paged(kp, vp, pt, page_size, slots)

@@ -39,6 +39,15 @@
  *                cu_seqlens_kv (by cu_seqlens_q when that is NULL)
  *                paged:      [num_pool_slots][num_heads_kv][head_dim]; token j of
  *                request b lives in slot page_table[b][j/p]*p + j%p ([V2] Eq. 22)
+ *       V (E4M3 only, v_layout = FP_V_COLS) stored transposed, each value
+ *                vector a column ([V2] §3.3 Eq. 16, first case):
+ *                contiguous: [num_heads_kv][head_dim][total_kv], element
+ *                (row t, head h, dim c) at (h*head_dim + c)*total_kv + t, every
+ *                K/V offset (and so total_kv) a multiple of 16;
+ *                paged: [num_pool_slots/p][num_heads_kv][head_dim][p] (p a
+ *                multiple of 64), token j of request b at
+ *                ((page*num_heads_kv + h)*head_dim + c)*p + j%p, page =
+ *                page_table[b][j/p]
  *       LSE      [total_q][num_heads_q] float, natural log
  *   - Element types: FP_F32 (float), FP_BF16 (bfloat16), FP_E4M3 (OCP E4M3FN
  *     with per-tensor descales c_q, c_k, c_v, [V2] §3.3 Eq. 15).  O is bf16
@@ -76,6 +85,11 @@ typedef enum {
 
 typedef enum { FP_F32 = 0, FP_BF16 = 1, FP_E4M3 = 2 } fp_dtype;
 
+/* Storage of V: rows (each token's vector contiguous, like K) or columns
+ * (each head's values transposed, [V2] §3.3 Eq. 16's column-major FP8 V,
+ * consumed without a copy; FP_E4M3 only). */
+typedef enum { FP_V_ROWS = 0, FP_V_COLS = 1 } fp_v_layout;
+
 /* One batch of prefill requests.  Built once per forward step and shared by
  * every layer ([V2] §3.4, serving integration).  A request has L_kv keys and
  * L_q <= L_kv queries; the queries are its last L_q positions, i.e. query i
@@ -102,6 +116,9 @@ typedef struct {
                                     or NULL: the same as cu_seqlens_q */
   const int32_t* cu_seqlens_kv_host; /* (host) the same values, or NULL; given together with
                                         cu_seqlens_kv; every L_kv >= its L_q */
+  int32_t v_layout;              /* fp_v_layout; FP_V_COLS needs FP_E4M3, and when paged a page
+                                    size that is a multiple of 64 and num_pool_slots a multiple of
+                                    it */
 } fp_problem;
 
 /* Block selection settings ([V2] §3.1 Eq. 3, §3.3 Eq. 20, defaults in §4.1:

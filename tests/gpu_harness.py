@@ -18,23 +18,25 @@ def fp():
 class GpuRun:
     """Device copies of a batch plus the library's buffers and results."""
 
-    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4, device="cuda"):
+    def __init__(self, batch, paged=None, alpha=0.1, sink=2, win=4, device="cuda", v_cols=False):
         F = fp()
         self.batch = batch
         self.paged = paged
         dt = TORCH_DT[batch.dtype]
         self.q = batch.q.to(device)
         if paged is None:
+            from block_sparse_long_mean_amd import synth
+
             self.k = batch.k.to(device)
-            self.v = batch.v.to(device)
+            self.v = (synth.v_columns(batch) if v_cols else batch.v).to(device)
             self.B = F.make_batch(batch.cu, batch.hq, batch.hkv, dt, cu_seqlens_kv=batch.cu_kv,
-                                  descale=batch.descale if batch.dtype == "e4m3" else None)
+                                  descale=batch.descale if batch.dtype == "e4m3" else None, v_cols=v_cols)
         else:
             self.k = paged.k_pool.to(device)
             self.v = paged.v_pool.to(device)
             self.B = F.make_batch(batch.cu, batch.hq, batch.hkv, dt, page_table=paged.page_table,
                                   page_size=paged.page_size, num_pool_slots=paged.num_slots,
-                                  cu_seqlens_kv=batch.cu_kv,
+                                  cu_seqlens_kv=batch.cu_kv, v_cols=v_cols,
                                   descale=batch.descale if batch.dtype == "e4m3" else None)
         self.params = F.select_params(alpha, sink, win)
         self.bufs = F.Buffers(self.B, self.params)

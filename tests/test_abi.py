@@ -206,3 +206,30 @@ def test_problem_struct_matches_the_header(tmp_path):
     P = fp.Problem
     assert got == [C.sizeof(P), P.softmax_scale.offset, P.cu_seqlens_kv.offset,
                    P.cu_seqlens_kv_host.offset]
+
+
+def test_column_major_v_checks():
+    fp = _fp()
+    p, cu = _problem(fp, lengths=(1008, 304), dtype=2, descale=0x3000)
+    p.v_layout = 1
+    assert _sizes(fp, p)[0] == 0, fp.lib_handle().fp_last_error()
+    p.v_layout = 2
+    assert _sizes(fp, p)[0] == -1
+    # an E4M3 layout only
+    p, cu = _problem(fp, lengths=(1008, 304), dtype=1)
+    p.v_layout = 1
+    assert _sizes(fp, p)[0] == -2
+    # contiguous: every K/V offset a multiple of 16
+    p, cu = _problem(fp, lengths=(1000, 304), dtype=2, descale=0x3000)
+    p.v_layout = 1
+    assert _sizes(fp, p)[0] == -2
+    # paged: pages a multiple of 64 tokens, the pool a whole number of pages
+    pt = np.zeros((2, 32), np.int32)
+    p, cu = _problem(fp, lengths=(1000, 300), dtype=2, descale=0x3000, page_table=pt.ctypes.data,
+                     page_size=64, max_pages=32, slots=64 * 40)
+    p.v_layout = 1
+    assert _sizes(fp, p)[0] == 0, fp.lib_handle().fp_last_error()
+    p.page_size, p.max_pages_per_req = 48, 32
+    assert _sizes(fp, p)[0] == -2
+    p.page_size, p.num_pool_slots = 64, 64 * 40 + 3
+    assert _sizes(fp, p)[0] == -2
