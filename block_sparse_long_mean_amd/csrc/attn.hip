@@ -284,7 +284,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   extern __shared__ __align__(16) char smem[];
   uint32_t* selbits = (uint32_t*)(smem + C::SELOFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: in a scalar register, addresses derived from it
+  // (LDS DMA destinations) need no per-instruction readfirstlane
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int2* units = (const int2*)(ws + wl.units);
   // logits in log2 units: x = s * sl (+ 7 for a mean that stands for 128 keys)

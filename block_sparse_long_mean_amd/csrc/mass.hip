@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
   const int64_t s = blockIdx.x;
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int nc = t.beta1 + 1;
   const float dq = DT == kE4M3 ? g.descale[0] : 1.f;

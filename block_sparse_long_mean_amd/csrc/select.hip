@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   const int64_t s = blockIdx.x;
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const float sl = g.scale * 1.4426950408889634f * (DT == kE4M3 ? g.descale[0] : 1.f);
   const int nc = t.beta1 + 1;  // blocks holding a key visible to some row
@@ -62,79 +62,70 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
       bl[ks] = pl[ks * 64 + lane];
     }
   };
-  // logits of the 128 rows x 32 blocks of column tile jt; per block (= lane
-  // column) the maximum and the sum of 2^(logit - max), logits in log2 units
+  // logits of the 128 rows x 32 blocks of column tile jt, 32 rows at a time;
+  // per block (= lane column) the running maximum of the raw products (sl > 0)
+  // and the sum of 2^(logit - max), logits in log2 units
   auto tile = [&](auto ragged_tag, int jt, const bf16x8 (&bh)[8], const bf16x8 (&bl)[8]) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
-    f32x16 acc[4];
+    float m = -INFINITY, sum = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      acc[rt] = f32x16{};
+      f32x16 acc = f32x16{};
       const uint16_t* arow = qh + (rt * 32 + col) * kQPitch + 8 * half;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         bf16x8 a = *(const bf16x8*)(arow + ks * 16);
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc[rt], 0, 0, 0);
-        acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc[rt], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc, 0, 0, 0);
         if constexpr (NQ == 2) {
           bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
-          acc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc[rt], 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc, 0, 0, 0);
         }
       }
-    }
-    // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4; padding
-    // rows of a ragged tile are masked out
-    if constexpr (RAGGED) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4; padding
+      // rows of a ragged tile are masked out
+      if constexpr (RAGGED) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) acc[rt][r] = -INFINITY;
-    }
-    // raw maximum (sl > 0), then one fma per exponent
-    float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 4) {
-        m0 = fmaxf(m0, fmaxf(acc[rt][r], acc[rt][r + 1]));
-        m1 = fmaxf(m1, fmaxf(acc[rt][r + 2], acc[rt][r + 3]));
+          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) acc[r] = -INFINITY;
       }
-    float mx = fmaxf(m0, m1);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      float m0 = fmaxf(acc[0], fmaxf(acc[1], acc[2])), m1 = fmaxf(acc[8], fmaxf(acc[9], acc[10]));
+      m0 = fmaxf(m0, fmaxf(acc[3], acc[4]));
+      m1 = fmaxf(m1, fmaxf(acc[11], acc[12]));
+      m0 = fmaxf(m0, fmaxf(acc[5], acc[6]));
+      m1 = fmaxf(m1, fmaxf(acc[13], acc[14]));
+      m0 = fmaxf(m0, fmaxf(acc[7], acc[15]));
+      const float mn = fmaxf(m, fmaxf(m0, m1));
+      const float msl = mn == -INFINITY ? 0.f : mn * sl;
+      float s0 = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -msl)), s1 = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        s0 += __builtin_amdgcn_exp2f(fmaf(acc[rt][r], sl, -mx));
-        s1 += __builtin_amdgcn_exp2f(fmaf(acc[rt][r + 1], sl, -mx));
+        s0 += __builtin_amdgcn_exp2f(fmaf(acc[r], sl, -msl));
+        s1 += __builtin_amdgcn_exp2f(fmaf(acc[r + 1], sl, -msl));
       }
-    float sum = s0 + s1;
-    sum += __shfl_xor(sum, 32, 64);
+      sum = s0 + s1;
+      m = mn;
+    }
+    // the other lane half holds the block's other 64 rows
+    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(sum, 32, 64);
+    const float mx = fmaxf(m, mo) * sl;
+    sum = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -mx)) + so * __builtin_amdgcn_exp2f(fmaf(mo, sl, -mx));
     const int J = jt * 32 + col;
     if (half == 0 && J < nc) {
       mJ[J] = mx;
       SJ[J] = sum;
     }
   };
-  // the next column tile's operands load while this one computes (two
-  // register sets, used alternately); only a request's last tile is ragged
-  // the first column tile's operands load while Q is staged
-  bf16x8 ah[8], al[8], bh[8], bl[8];
-  if (wave < njt) kb_load(wave, ah, al);
+  // one register set of operands per wave; the first column tile's load is in
+  // flight while Q is staged
+  bf16x8 bh[8], bl[8];
+  if (wave < njt) kb_load(wave, bh, bl);
   stage_q<DT>(g, c, t, q, qh, ql);
   __syncthreads();
   auto sweep = [&](auto ragged_tag) {
-    int jt = wave;
-    while (jt < njt) {
-      if (jt + 4 < njt) kb_load(jt + 4, bh, bl);
-      tile(ragged_tag, jt, ah, al);
-      jt += 4;
-      if (jt >= njt) break;
-      if (jt + 4 < njt) kb_load(jt + 4, ah, al);
+    for (int jt = wave; jt < njt; jt += 4) {
+      if (jt != wave) kb_load(jt, bh, bl);
       tile(ragged_tag, jt, bh, bl);
-      jt += 4;
     }
   };
   if (nrows < kRows)
