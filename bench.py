@@ -365,7 +365,7 @@ def main():
     ap.add_argument("--config", default=configs.L128K.name, choices=sorted(configs.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / fp8 / alpha variants")
-    ap.add_argument("--cpu-segments", type=int, default=256)
+    ap.add_argument("--cpu-segments", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     ap.add_argument("--sweep", action="store_true",
