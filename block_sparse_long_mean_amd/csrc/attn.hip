@@ -799,6 +799,19 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
       }
     } else {
+    // e4m3: the denominator of Eq. 15 sums the rounded P; one more MFMA per
+    // step with an all-ones A operand forms those sums (every row of the
+    // product is the column sum of P^T), in place of decoding P back on the
+    // VALU.  Only element 0 is read, so the rescale touches only it.
+    f32x16 lacc = f32x16{};
+    const Op ones = [] {
+      Op o{};
+      if constexpr (DT == kE4M3) {
+#pragma unroll
+        for (int w = 0; w < 8; ++w) o[w] = 0x38383838;  // e4m3 1.0
+      }
+      return o;
+    }();
     // per-lane DMA offsets within a 64-row tile (bf16/e4m3): instruction q of
     // wave w fills rows 16w + RPI q + lane / CPR, chunk lane % CPR, which holds
     // the row's logical chunk (lane % CPR) ^ swizzle(row)
@@ -1121,7 +1134,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         } else if (__any(m_step > m_i + kTau)) {
           const float m_new = fmaxf(m_i, m_step);
           const float resc = __builtin_amdgcn_exp2f(m_i - (m_new == -INFINITY ? 0.f : m_new));
-          l_i *= resc;
+          lacc[0] *= resc;
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -1144,15 +1157,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         // P^T as the B operands of O^T += V^T P^T
         Op pf[C::NM1];
         if constexpr (DT == kE4M3) {
-          float psum = 0.f;
           i32x8 b;
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int jt = w >> 2, r = (w & 3) * 4;
             const uint32_t word = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]) |
                                   (f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]) << 16);
-            const f32x4 back = e4m3x4_to_f32(word);  // the denominator sums the rounded P (Eq. 15)
-            psum += (back[0] + back[1]) + (back[2] + back[3]);
             b[w] = (int)word;
           }
           if constexpr (VC) {
@@ -1172,7 +1182,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             b = nb;
           }
           pf[0] = b;
-          l_i += psum;
         } else {
           float psum = 0.f;
 #pragma unroll
@@ -1213,6 +1222,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             for (int m1 = 0; m1 < C::NM1; ++m1) oacc[nt] = mma<DT>(v_op(vt, nt, m1), pf[m1], oacc[nt]);
           }
         }
+        lacc = mma<DT>(ones, pf[0], lacc);  // row sums of the rounded P
       } else {
         // Two halves of 32 keys (logit tile jt), each an online-softmax update
         // of its own.  The VALU work of half 0 overlaps the MFMAs of half 1's
@@ -1299,6 +1309,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if constexpr (!DENSE) {
       while (cur < it1) run_step(KChunk{});
     }
+    // e4m3: the complete row sum sits in both lane halves; the epilogue adds halves
+    if constexpr (DT == kE4M3) l_i = half ? 0.f : lacc[0];
 
     }
 
