@@ -1320,7 +1320,38 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if (tid == 0) sh_unit = ticket < own_hi - own_lo ? own_hi - 1 - ticket : steal(xcd + 1);
     const bool bad = __syncthreads_or(err != 0) != 0;
     const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
-    if (un.nsplit == 1) {
+    if (DT == kBF16 && un.nsplit == 1 && !bad) {
+      // bf16: the wave's 32 output rows pass through LDS (the K buffers, which
+      // nothing reads after the unit's last barrier; rows padded to 272 bytes
+      // so that the 32 rows' writes spread over the banks), and every store
+      // then writes whole 16-byte pieces of 4 consecutive rows instead of
+      // 8-byte pieces of 32.
+      char* ob = smem + PipeL::K0 + wave * 32 * 272;
+      const float inv = cvs / l_tot;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int n0 = nt * 32 + 8 * b4 + 4 * half;
+          const uint32_t w0 = f32_to_bf16_bits(oacc[nt][4 * b4] * inv) |
+                              ((uint32_t)f32_to_bf16_bits(oacc[nt][4 * b4 + 1] * inv) << 16);
+          const uint32_t w1 = f32_to_bf16_bits(oacc[nt][4 * b4 + 2] * inv) |
+                              ((uint32_t)f32_to_bf16_bits(oacc[nt][4 * b4 + 3] * inv) << 16);
+          *(uint2*)(ob + col * 272 + n0 * 2) = make_uint2(w0, w1);
+        }
+      if (row_ok && lse && half == 0)
+        lse[(c.row0 + qi) * g.hq + head] = (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4), c16 = lane & 15;
+        if (wave * 32 + r < t.nrows) {
+          const int64_t pr = c.I * kRows + wave * 32 + r;
+          const int64_t orow = (c.row0 + (pr >> g.log2g)) * g.hq + c.h * g.g + (int)(pr & (g.g - 1));
+          *(uint4*)((char*)out + orow * kD * 2 + c16 * 16) = *(const uint4*)(ob + r * 272 + c16 * 16);
+        }
+      }
+    } else if (un.nsplit == 1) {
       if (row_ok) {
         if (!bad) {
           const float inv = cvs / l_tot;
