@@ -203,7 +203,7 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
   w.work = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.wscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
   w.uscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
-  w.units = o; o = align256(o + (size_t)hg.n_seg * sp.umax * 8);
+  w.units = o; o = align256(o + (size_t)hg.n_seg * sp.umax * sizeof(UnitRec));
   w.part_o = o; o = align256(o + (sp.umax > 1 ? (size_t)hg.n_seg * sp.umax * kRows * kD * 4 : 0));
   w.part_ml = o; o = align256(o + (sp.umax > 1 ? (size_t)hg.n_seg * sp.umax * 2 * kRows * 4 : 0));
   w.total = o;

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   // (LDS DMA destinations) need no per-instruction readfirstlane
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int2* units = (const int2*)(ws + wl.units);
+  const UnitRec* units = (const UnitRec*)(ws + wl.units);
   // logits in log2 units: x = s * sl (+ 7 for a mean that stands for 128 keys)
   const float sl = g.scale * 1.4426950408889634f *
                    (DT == kE4M3 ? g.descale[0] * g.descale[1] : 1.f);
@@ -367,17 +367,25 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if (u < 0) break;
     int ticket = 0;
     if (tid == 0) ticket = atomicAdd(&g.hdr->xcd_counter[xcd][0], 1);
-    const int2 ud = units[u];
-    const Unit un{ud.x, ud.y & 0xffff, ud.y >> 16};
-    const SegCoord c = seg_coord(g, un.s);
+    const UnitRec ur = units[u];
+    const Unit un{ur.s, ur.split_ns & 0xffff, ur.split_ns >> 16};
+    SegCoord c;
+    c.b = ur.b;
+    c.h = ur.h;
+    c.I = ur.I;
+    c.L = ur.L;
+    c.Lq = ur.Lq;
+    c.off = ur.off;
+    c.row0 = ur.row0;
+    c.kv0 = ur.kv0;
     const TileGeo t = tile_geo(g, c);
     uint32_t err = 0;
     int T, seg0 = 0;
     if constexpr (DENSE) {
       T = t.t1 / kTile + 1;
     } else {
-      seg0 = cu[un.s];
-      T = cu[un.s + 1] - seg0;
+      seg0 = ur.seg0;
+      T = ur.T;
       if (T < 0 || T > 2 * (t.beta1 + 1)) {
         err |= kErrIdx;
         T = 0;
@@ -406,13 +414,13 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       vbase = (const char*)v + base;
       kvbytes = (uint64_t)(g.num_slots - 1) * rowstride + kD * EB;
     }
-    const uint64_t mbase = ((uint64_t)g.blk_base[c.b] * g.hkv + c.h) * kD * EB;
+    const uint64_t mbase = ((uint64_t)ur.blk_base * g.hkv + c.h) * kD * EB;
     const char* kmbase = means + ml.kop + mbase;
     const char* vmbase = means + ml.vop + mbase;
     // transposed V (e4m3): this head's dim rows, and the transposed correction
     // operands ([chunk][head][dim][64 blocks]) of the request's first chunk
     const char* vtbase = (const char*)v + (AM == kContig ? (uint64_t)c.h * kD * g.vrow + c.kv0 : 0);
-    const char* vtmbase = means + ml.vop + (uint64_t)((g.blk_base[c.b] >> 6) * g.hkv + c.h) * kD * kChunk;
+    const char* vtmbase = means + ml.vop + (uint64_t)((ur.blk_base >> 6) * g.hkv + c.h) * kD * kChunk;
     const uint64_t mbytes = (uint64_t)(((t.beta + kChunk - 1) / kChunk) * kChunk) * rowstride;
 
     if (NC > 0) {

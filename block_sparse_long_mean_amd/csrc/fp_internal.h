@@ -68,6 +68,20 @@ struct MeansLayout {
   size_t total;
 };
 
+// One attention work unit as the scheduler writes it: everything a unit needs
+// to start, in one 64-byte record (a single load instead of a chain of
+// dependent lookups of segment offsets and CSR bounds).
+struct UnitRec {
+  int32_t s;          // segment
+  int32_t split_ns;   // split | nsplit << 16
+  int32_t seg0, T;    // CSR offset and listed tile count (sparse)
+  int32_t b, h, I;    // request, kv head, query tile
+  int32_t L, Lq, off; // key length, query length, first query position
+  int32_t row0, kv0;  // first Q row, first K/V row (contiguous)
+  int32_t blk_base;   // first (padded) block of the request
+  int32_t pad[3];
+};
+
 // Layout of the workspace (byte offsets).
 struct WsLayout {
   size_t hdr, seg_off, blk_base, counts, scan_part, bits, work, wscan, uscan, units, part_o, part_ml, total;

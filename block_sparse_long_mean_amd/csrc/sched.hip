@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void sched_count_kernel(Geo g, const int32_t* 
 // wscan / uscan: exclusive prefix sums of work and split counts ([n_seg + 1]).
 __global__ __launch_bounds__(256) void sched_place_kernel(Geo g, const int32_t* __restrict__ wscan,
                                                           const int32_t* __restrict__ uscan,
-                                                          const int32_t* __restrict__ nsplit, int2* units) {
+                                                          const int32_t* __restrict__ nsplit,
+                                                          const int32_t* __restrict__ cu, UnitRec* units) {
   const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = g.n_seg;
   const int64_t wtot = max(1, wscan[n]);
@@ -66,7 +67,24 @@ __global__ __launch_bounds__(256) void sched_place_kernel(Geo g, const int32_t* 
     for (int y = x + 1; y < kXcds; ++y) g.hdr->xcd_start[y] = uscan[n];
   const int U = nsplit[s];
   const int base = uscan[s];
-  for (int u = 0; u < U; ++u) units[base + u] = make_int2((int)s, u | (U << 16));
+  const SegCoord c = seg_coord(g, s);
+  UnitRec r{};
+  r.s = (int32_t)s;
+  r.seg0 = cu ? cu[s] : 0;
+  r.T = cu ? cu[s + 1] - cu[s] : 0;
+  r.b = c.b;
+  r.h = c.h;
+  r.I = (int32_t)c.I;
+  r.L = c.L;
+  r.Lq = c.Lq;
+  r.off = c.off;
+  r.row0 = (int32_t)c.row0;
+  r.kv0 = (int32_t)c.kv0;
+  r.blk_base = g.blk_base[c.b];
+  for (int u = 0; u < U; ++u) {
+    r.split_ns = u | (U << 16);
+    units[base + u] = r;
+  }
 }
 
 hipError_t launch_sched(const Geo& g, const WsLayout& wl, char* ws, const int32_t* cu, int dense,
@@ -76,14 +94,14 @@ hipError_t launch_sched(const Geo& g, const WsLayout& wl, char* ws, const int32_
   int32_t* wscan = (int32_t*)(ws + wl.wscan);
   int32_t* uscan = (int32_t*)(ws + wl.uscan);
   int32_t* part = (int32_t*)(ws + wl.scan_part);
-  int2* units = (int2*)(ws + wl.units);
+  UnitRec* units = (UnitRec*)(ws + wl.units);
   const unsigned nb = (unsigned)((g.n_seg + 255) / 256);
   sched_count_kernel<<<nb, 256, 0, st>>>(g, cu, dense, correction, sp, work, nsplit);
   hipError_t e = launch_scan(work, g.n_seg, wscan, part, st);
   if (e != hipSuccess) return e;
   e = launch_scan(nsplit, g.n_seg, uscan, part, st);
   if (e != hipSuccess) return e;
-  sched_place_kernel<<<nb, 256, 0, st>>>(g, wscan, uscan, nsplit, units);
+  sched_place_kernel<<<nb, 256, 0, st>>>(g, wscan, uscan, nsplit, dense ? nullptr : cu, units);
   return hipGetLastError();
 }
 
