@@ -193,3 +193,34 @@ def test_bad_idx_is_flagged():
     torch.cuda.synchronize()
     run.attn()
     assert run.device_error() & 2
+
+
+@pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "bf16"), (16, 8, "bf16"), (32, 2, "bf16"), (8, 8, "e4m3")])
+def test_group_sizes(hq, hkv, dtype):
+    """GQA group sizes other than 8: g = 1 (a 128-row tile spans two key tiles,
+    so rows of the first half see nothing in the second; masked steps with fully
+    masked rows), g = 2 and g = 16; full CSR and sampled attention."""
+    _print_case("group", hq=hq, hkv=hkv, dtype=dtype)
+    b = synth.make_batch([1000, 2500, 333], hq, hkv, 128, seed=37, dtype="bf16", clusters=True, diag_bias=True)
+    if dtype == "e4m3":
+        b = synth.to_e4m3(b)
+    run = GpuRun(b)
+    cu, idx = run.select()
+    P = oracle_for(run)
+    n, amb = compare_csr(P, cu, idx, 0.1, 2, 4)
+    print(f"  CSR: {n} segments, {amb} band differences")
+    segs = sample_segments(P, 64, seed=11)
+    tmax, tmean = TOL[dtype]
+    for corr in (True, False):
+        out, lse = run.attn(correction=corr)
+        if dtype == "e4m3":
+            check_e4m3(P, out, lse, segs, cu, idx, corr, tmax, tmean)
+        else:
+            mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
+            print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
+            assert mx <= tmax and mean <= tmean
+    out, lse = run.attn(dense=True)
+    mx, mean, _ = compare_attn(P, out, lse, segs, dense=True)
+    print(f"  dense: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= tmax and mean <= tmean
+    assert run.device_error() == 0
