@@ -233,3 +233,20 @@ def test_column_major_v_checks():
     assert _sizes(fp, p)[0] == -2
     p.page_size, p.num_pool_slots = 64, 64 * 40 + 3
     assert _sizes(fp, p)[0] == -2
+
+
+def test_empty_batch_launches_nothing():
+    """Every request empty: the calls return before launching anything."""
+    fp = _fp()
+    lib = fp.lib_handle()
+    p, cu = _problem(fp, lengths=(0, 0))
+    sp = fp.select_params()
+    st, s = _sizes(fp, p, sp)
+    assert st == 0 and s.n_segments == 0
+    dummy = C.c_void_p(0x1000)
+    ws = max(1, s.workspace_bytes)
+    assert lib.fp_select(C.byref(p), C.byref(sp), dummy, dummy, dummy, dummy, dummy, max(1, s.idx_capacity),
+                         dummy, None, dummy, ws, None) == 0
+    assert lib.fp_sparse_attn(C.byref(p), C.byref(sp), dummy, dummy, dummy, dummy, dummy, dummy, 1, dummy, None,
+                              dummy, ws, None) == 0
+    assert lib.fp_dense_attn(C.byref(p), dummy, dummy, dummy, dummy, None, dummy, ws, None) == 0

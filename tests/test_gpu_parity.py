@@ -224,3 +224,49 @@ def test_group_sizes(hq, hkv, dtype):
     print(f"  dense: max {mx:.3e} mean {mean:.3e}")
     assert mx <= tmax and mean <= tmean
     assert run.device_error() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_edge_lengths(dtype):
+    """Requests of 1, 2, 63, 64, 65, 127, 128, 129, 255 and 257 tokens (tile and
+    block edges, single-token requests) in one batch: full CSR, every segment."""
+    lengths = [1, 2, 63, 64, 65, 127, 128, 129, 255, 257]
+    _print_case("edge lengths", dtype=dtype)
+    b = synth.make_batch(lengths, 8, 2, 128, seed=41, dtype=dtype, clusters=True, diag_bias=True)
+    run = GpuRun(b, alpha=0.1, sink=1, win=1)
+    cu, idx = run.select()
+    P = oracle_for(run)
+    compare_csr(P, cu, idx, 0.1, 1, 1)
+    segs = list(range(P.num_segments()))
+    tmax, tmean = TOL[dtype]
+    for corr in (True, False):
+        out, lse = run.attn(correction=corr)
+        mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
+        print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
+        assert mx <= tmax and mean <= tmean
+    out, lse = run.attn(dense=True)
+    mx, mean, _ = compare_attn(P, out, lse, segs, dense=True)
+    assert mx <= tmax and mean <= tmean
+    assert run.device_error() == 0
+
+
+def test_longest_request():
+    """The longest request the library takes (8192 blocks = 1,048,576 tokens), MHA
+    (g = 1): the scoring kernel's per-block arrays and the attention kernel's
+    selected-block bitmask at their largest; sampled segments."""
+    L = 8192 * 128
+    _print_case("longest request", L=L)
+    b = synth.make_batch([L], 1, 1, 128, seed=43, dtype="bf16", clusters=True, diag_bias=True)
+    run = GpuRun(b)
+    assert run.sizes.max_blocks == 8192
+    cu, idx = run.select()
+    P = oracle_for(run)
+    nseg = P.num_segments()
+    segs = [0, 1, nseg // 2, nseg - 2, nseg - 1]
+    n, amb = compare_csr(P, cu, idx, 0.1, 2, 4, segs=segs)
+    print(f"  CSR: {n} sampled segments, {amb} band differences; entries {len(idx)}")
+    out, lse = run.attn(correction=True)
+    mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=True)
+    print(f"  attention: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
+    assert mx <= 2e-2 and mean <= 2e-3
+    assert run.device_error() == 0
