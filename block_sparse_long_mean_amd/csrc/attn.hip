@@ -423,6 +423,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const char* vtmbase = means + ml.vop + (uint64_t)((ur.blk_base >> 6) * g.hkv + c.h) * kD * kChunk;
     const uint64_t mbytes = (uint64_t)(((t.beta + kChunk - 1) / kChunk) * kChunk) * rowstride;
 
+    // listed tiles of the first 64 steps, one per lane (step it reads lane it)
+    int vidx = 0;
+    if constexpr (!DENSE) {
+      if (lane < T) vidx = idx[seg0 + T - 1 - lane];
+    }
     if (NC > 0) {
       for (int w = tid; w <= (t.beta >> 5) + 2; w += 256) selbits[w] = 0;
       __syncthreads();
@@ -432,6 +437,20 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     }
     __syncthreads();
+    // correction chunks with work (a visible block that is not listed): one
+    // bit per chunk, chunks 0-63 and 64-127 (beta <= 8192 blocks)
+    uint64_t todo_lo = 0, todo_hi = 0;
+    if (NC > 0) {
+      auto chunk_has_work = [&](int ch) -> bool {
+        if (ch >= NC) return false;
+        const int n = min(kChunk, t.beta - ch * kChunk);
+        const uint32_t m0 = n >= 32 ? 0xffffffffu : (1u << n) - 1u;
+        const uint32_t m1 = n >= 64 ? 0xffffffffu : n <= 32 ? 0u : (1u << (n - 32)) - 1u;
+        return ((~selbits[2 * ch] & m0) | (~selbits[2 * ch + 1] & m1)) != 0u;
+      };
+      todo_lo = __ballot(chunk_has_work(lane));
+      todo_hi = __ballot(chunk_has_work(lane + 64));
+    }
 
     // ---- the wave's 32 query rows: B operand of S^T = K Q^T, kept in registers
     const int row_in_tile = wave * 32 + col;
@@ -468,18 +487,15 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     for (int nt = 0; nt < 4; ++nt) oacc[nt] = f32x16{};
 
     // ---- steps: listed tiles backwards (Eq. 17), then correction chunks
-    auto chunk_todo = [&](int ch) -> bool {
-      const int j0 = ch * kChunk, j1 = min(j0 + kChunk, t.beta);
-      for (int J = j0; J < j1; J += 32) {
-        const int n = min(32, j1 - J);
-        const uint32_t mask = n == 32 ? 0xffffffffu : ((1u << n) - 1u);
-        if ((~selbits[J >> 5]) & mask) return true;
-      }
-      return false;
-    };
+    // the first step at or after it that has work: a listed tile, or a
+    // correction chunk whose bit is set
     auto next_step = [&](int it) -> int {
-      while (it < it1 && it >= T && !chunk_todo(it - T)) ++it;
-      return __builtin_amdgcn_readfirstlane(it);  // uniform: every lane reads the same bits
+      if (it < T || it >= it1) return it;
+      const int ch = it - T;
+      const uint64_t lo = ch < 64 ? todo_lo & (~0ull << ch) : 0ull;
+      const uint64_t hi = ch < 64 ? todo_hi : ch < 128 ? todo_hi & (~0ull << (ch - 64)) : 0ull;
+      const int nc = lo ? __builtin_ctzll(lo) : hi ? 64 + __builtin_ctzll(hi) : (1 << 20);
+      return min(T + nc, it1);
     };
     // strictly ascending list: a split also checks the entry its predecessor saw last
     int prev_tile = 1 << 30;
@@ -490,7 +506,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       if constexpr (DENSE) {
         return T - 1 - it;
       } else {
-        int p = __builtin_amdgcn_readfirstlane(idx[seg0 + T - 1 - it]);
+        int p = it < 64 ? __builtin_amdgcn_readlane(vidx, it) : __builtin_amdgcn_readfirstlane(idx[seg0 + T - 1 - it]);
         if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
           err |= kErrIdx;
           p = 0;
@@ -500,10 +516,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
-    // Output rescaling is deferred until a row's max exceeds the max that its
-    // accumulators are scaled to by more than 2^kTau (bf16 / fp32: exact up
-    // to rounding, probabilities stay below 2^8).  e4m3 quantises P against
-    // the running max itself (Eq. 15), so there kTau is 0.
+    // One-step paths (e4m3, fp32): output rescaling is deferred until a row's
+    // max exceeds the max that its accumulators are scaled to by more than
+    // 2^kTau (fp32: exact up to rounding, probabilities stay below 2^8).  e4m3
+    // quantises P against the running max itself (Eq. 15), so there kTau is 0.
+    // The bf16 pipeline below keeps its own reference maximum.
     constexpr float kTau = DT == kE4M3 ? 0.f : 8.f;
     bool fresh = true;  // nothing accumulated yet: the first max needs no rescale
 
@@ -544,8 +561,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         if (it < T) {
           j0 = p * kTile;
           if constexpr (AM == kContig) {
-            const uint64_t o = (uint64_t)j0 * rowstride;
-            r = make_rsrc(base + o, kvbytes > o ? kvbytes - o : 0);
+            // bytes from the tile's first row to the end of the request's last
+            // row, or no limit when the whole tile lies inside the request
+            const int rem = c.L - 1 - j0;
+            const uint32_t n = rem >= kTile ? 0xffffffffu : rem < 0 ? 0u : (uint32_t)rem * rowstride + kD * EB;
+            r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (uint64_t)j0 * rowstride, (short)0,
+                                                  (int)n, kBufFlags);
           } else if constexpr (AM == kPagedTile) {
             const int pg = j0 / g.page_size;
             const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
@@ -562,8 +583,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             rows = true;
           }
         } else {
+          // a whole chunk of 64 means rows: the means are padded to full chunks
           const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
-          r = make_rsrc(mb + o, mbytes > o ? mbytes - o : 0);
+          r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(mb) + o, (short)0, (int)0xffffffffu, kBufFlags);
         }
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
@@ -633,10 +655,26 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           for (int g2 = 0; g2 < 4; ++g2) ring[g2] = vread(vb, g2 >> 1, 2 + (g2 & 1));
         }
 
-        // softmax state of the current half
-        float ma = 0.f, mh = 0.f, m_new = 0.f, m_use = 0.f, resc = 1.f, psum = 0.f;
+        // Softmax state.  The weights of a half step are first taken against
+        // the reference maximum mref (the row's running maximum m_i) with no
+        // reduction at all; only when some lane's 16 weights sum above 2^8 (a
+        // new maximum more than that far up, or the first visible key of a row,
+        // for which mref is -1e30 so that every finite weight overflows) does
+        // the wave take the exact maximum of the half, exchange it between the
+        // lane halves, and compute the weights again.  Exact up to rounding:
+        // the weights stay at most 2^8 times their true scale.
+        float mref = -1e30f, resc = 1.f, psum = 0.f;
         bool need = false;
-        f32x4 pv[2];  // correction offsets of 8 registers, read one piece ahead
+        uint32_t pw[8];  // the half's weights as bf16 pairs
+        f32x4 pv[2];     // correction offsets of 8 registers, read one piece ahead
+        auto weight = [&](auto kind_tag, float x, float m) -> float {
+          constexpr int KIND = decltype(kind_tag)::value;
+          return __builtin_amdgcn_exp2f(KIND == 2 ? x + (kOff - m) : fmaf(x, sl, kOff - m));
+        };
+        auto pack = [](float a, float b) -> uint32_t {
+          const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+          return __builtin_bit_cast(uint32_t, v);
+        };
         // piece k (0..15) of the softmax of a 32-key half sv (logit tile jt)
         auto sub = [&](auto kind_tag, f32x16& sv, int jt, int k, Op* ph, const f32x4* penp) {
           constexpr int KIND = decltype(kind_tag)::value;
@@ -663,56 +701,46 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             }
 #pragma unroll
             for (int r = r0; r < r0 + 8; ++r) pin(sv[r]);
-          } else if (k == 3) {
-            ma = fmaxf(sv[0], fmaxf(sv[1], sv[2]));
-            ma = fmaxf(ma, fmaxf(sv[3], sv[4]));
-            ma = fmaxf(ma, fmaxf(sv[5], sv[6]));
-            ma = fmaxf(ma, sv[7]);
-            pin(ma);
-          } else if (k == 4) {
-            float mb = fmaxf(sv[8], fmaxf(sv[9], sv[10]));
-            mb = fmaxf(mb, fmaxf(sv[11], sv[12]));
-            mb = fmaxf(mb, fmaxf(sv[13], sv[14]));
-            mh = fmaxf(ma, fmaxf(mb, sv[15]));
-            pin(mh);
-          } else if (k == 5) {
-            // the other lane half holds the same query row
-            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
-            const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
-            need = __any(m_half > m_i + kTau);
-            m_new = need ? fmaxf(m_i, m_half) : m_i;
-            m_use = m_new == -INFINITY ? 0.f : m_new;
-            resc = __builtin_amdgcn_exp2f(m_i - m_use);
-            pin(m_use);
-            pin(resc);
-          } else if (k < 14) {
-            const int r0 = (k - 6) * 2;
+          } else if (k < 14 && k % 3 != 2) {
+            // weights 2(k-3) and 2(k-3)+1: bf16 pair and the fp32 row sum
+            // (plain adds: they issue beside the MFMAs, bf16 dot products would not)
+            const int r = 2 * (k - 3 - (k - 3) / 3);
+            const float e0 = weight(kind_tag, sv[r], mref), e1 = weight(kind_tag, sv[r + 1], mref);
+            pw[r >> 1] = pack(e0, e1);
+            psum = k == 3 ? e0 + e1 : psum + e0 + e1;
+            pin(pw[r >> 1]);
+            pin(psum);
+          } else if (k == 14) {
+            need = __any(!(psum <= 256.f));
+            resc = 1.f;
+            if (need) {
+              float mh = sv[0];
 #pragma unroll
-            for (int r = r0; r < r0 + 2; ++r) {
-              sv[r] = __builtin_amdgcn_exp2f(KIND == 2 ? sv[r] + (kOff - m_use) : fmaf(sv[r], sl, kOff - m_use));
-              pin(sv[r]);
-            }
-          } else {
-            // bf16 P and the fp32 row sum (plain adds: they issue beside the
-            // MFMAs, where bf16 dot products would not)
-            const int q2 = k - 14;
-            bf16x8 bv;
-            float ps2 = 0.f;
+              for (int r = 1; r < 16; ++r) mh = fmaxf(mh, sv[r]);
+              mh = fmaxf(mh, __shfl_xor(mh, 32, 64));  // the other lane half holds the same query row
+              const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
+              const float m_new = fmaxf(m_i, m_half);
+              const float m_use = m_new == -INFINITY ? 0.f : m_new;
+              resc = __builtin_amdgcn_exp2f(m_i - m_use);
+              m_i = m_new;
+              mref = m_new == -INFINITY ? -1e30f : m_new;
+              psum = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bv[e] = static_cast<__bf16>(sv[8 * q2 + e]);
-              ps2 += sv[8 * q2 + e];
+              for (int r = 0; r < 16; r += 2) {
+                const float e0 = weight(kind_tag, sv[r], m_use), e1 = weight(kind_tag, sv[r + 1], m_use);
+                pw[r >> 1] = pack(e0, e1);
+                psum += e0 + e1;
+              }
             }
-            psum += ps2;
-            ph[q2] = bv;
-            pin(bv);
+            ph[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+            ph[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+            pin(ph[0]);
+            pin(ph[1]);
             pin(psum);
           }
         };
         auto commit = [&]() {
           l_i = fmaf(l_i, resc, psum);
-          m_i = m_new;
-          psum = 0.f;
           if (need && !fresh) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
