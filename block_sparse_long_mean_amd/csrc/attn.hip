@@ -535,8 +535,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       // C(n): K(n+1) and V(n) (loaded one iteration earlier) become visible,
       // K(n+2) and V(n+1) are loaded.  K tiles alternate between two buffers
       // by step parity, V tiles likewise, correction offsets rotate through
-      // three tables.  The first iteration's D(-1) multiplies a copy of V(0)
-      // by P = 0 (adding exact zeros); the last iteration's A(n+1) is computed
+      // three tables.  The first iteration's D(-1) multiplies V(0) by P = 0
+      // (adding exact zeros); the last iteration's A(n+1) is computed
       // on stale data and not used.
       using PL = PipeL;
       auto kread = [&](const char* kb, int jt, int m) -> Op {
@@ -627,7 +627,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         dma_bf16(std::true_type{}, PL::K0, cur, cur_tile);
         pen_bf16(0, cur);
         dma_bf16(std::false_type{}, PL::V0, cur, cur_tile);
-        dma_bf16(std::false_type{}, PL::V1, cur, cur_tile);  // read by D(-1), with P = 0
         if (nxt < it1) {
           dma_bf16(std::true_type{}, PL::K1, nxt, nxt_tile);
           pen_bf16(1, nxt);
@@ -649,8 +648,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             s0 = mma<DT>(a, qf[m], s0);
             __builtin_amdgcn_sched_barrier(0);
           }
-          // operands of D(-1): V(0) again, times P = 0
-          const char* vb = smem + PL::V1 + lane_v;
+          // operands of D(-1): V(0), times P = 0
+          const char* vb = smem + PL::V0 + lane_v;
 #pragma unroll
           for (int g2 = 0; g2 < 4; ++g2) ring[g2] = vread(vb, g2 >> 1, 2 + (g2 & 1));
         }
@@ -750,11 +749,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           fresh = false;
         };
 
+        int first = 1;
         auto iter = [&](auto kind_tag) {
           const char* kbc = smem + (bk ? PL::K1 : PL::K0) + lane_k;  // K(n)
           const char* kbn = smem + (bk ? PL::K0 : PL::K1) + lane_k;  // K(n+1)
           const char* vbc = smem + (bk ? PL::V1 : PL::V0) + lane_v;  // V(n)
-          const char* vbp = smem + (bk ? PL::V0 : PL::V1) + lane_v;  // V(n-1)
+          const char* vbp = smem + ((bk | first) ? PL::V0 : PL::V1) + lane_v;  // V(n-1); V(0) for D(-1)
           const f32x4* penp = (const f32x4*)(smem + PL::PEN + ps * 256) + half * 8;
           auto fetch = [&](int gs) -> Op {
             if (gs < 8) return vread(vbp, gs >> 1, 2 + (gs & 1));
@@ -812,6 +812,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           commit();
           bk ^= 1;
           ps = ps == 2 ? 0 : ps + 1;
+          first = 0;
           cur = nxt;
           cur_tile = nxt_tile;
           nxt = nxt2;
@@ -1361,7 +1362,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       // nothing reads after the unit's last barrier; rows padded to 272 bytes
       // so that the 32 rows' writes spread over the banks), and every store
       // then writes whole 16-byte pieces of 4 consecutive rows instead of
-      // 8-byte pieces of 32.
+      // 8-byte pieces of 32.  Each wave reads back only its own rows, and a
+      // wave's LDS accesses complete in order, so no barrier sits between.
       char* ob = smem + PipeL::K0 + wave * 32 * 272;
       const float inv = cvs / l_tot;
 #pragma unroll
@@ -1377,7 +1379,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
       if (row_ok && lse && half == 0)
         lse[(c.row0 + qi) * g.hq + head] = (m_i + __builtin_amdgcn_logf(l_tot) - kOff) * 0.6931471805599453f;
-      __syncthreads();
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + (lane >> 4), c16 = lane & 15;
