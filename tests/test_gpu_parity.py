@@ -270,3 +270,35 @@ def test_longest_request():
     print(f"  attention: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
     assert mx <= 2e-2 and mean <= 2e-3
     assert run.device_error() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_long_tile_lists(dtype):
+    """alpha = 0 keeps every causal block, so late tiles list more than 64 tiles:
+    the attention kernel holds the list of a unit's first 64 steps in a register
+    and reads longer lists from memory.  Both parts are checked against the
+    oracle on the segments with the longest lists, and against dense attention."""
+    b = _small(dtype, lengths=(6000, 4100), seed=17)
+    _print_case("long tile lists", dtype=dtype)
+    run = GpuRun(b, alpha=0.0, sink=2, win=4)
+    cu, idx = run.select()
+    P = oracle_for(run)
+    sizes = np.diff(cu)
+    assert sizes.max() > 64, int(sizes.max())
+    segs = sorted(set(np.argsort(sizes)[-12:].tolist()) | {0})
+    compare_csr(P, cu, idx, 0.0, 2, 4, segs=segs)
+    tmax, tmean = TOL[dtype]
+    for corr in (True, False):
+        out, lse = run.attn(correction=corr)
+        if dtype == "e4m3":
+            check_e4m3(P, out, lse, segs, cu, idx, corr, tmax, tmean)
+        else:
+            mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
+            print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}", flush=True)
+            assert mx <= tmax and mean <= tmean
+    if dtype == "bf16":
+        s_out, _ = run.attn(correction=True)
+        d_out, _ = run.attn(dense=True)
+        diff = (s_out.float() - d_out.float()).abs()
+        assert float(diff.max()) < 1e-2 and float(diff.mean()) < 1e-4
+    assert run.device_error() == 0
