@@ -157,6 +157,7 @@ MeansLayout means_layout(const fp_problem* p, const HostGeo& hg) {
   m.klo = o; o = align256(o + rows * 2);
   m.kop = o; o = align256(o + rows * elem_size(p->dtype));
   m.vop = o; o = align256(o + rows * elem_size(p->dtype));
+  m.kbnd = o; o = align256(o + (size_t)hg.nb_pad * p->num_heads_kv * 4);
   m.total = o;
   return m;
 }

@@ -65,6 +65,7 @@ struct MeansLayout {
   size_t kbar32, vbar32;  // float [nb_pad][hkv][128]
   size_t khi, klo;        // bf16, MFMA B-operand order: [nb_pad/32][hkv][8][64][8]
   size_t kop, vop;        // element dtype, [nb_pad][hkv][128]: operands of correction steps
+  size_t kbnd;            // float [nb_pad][hkv]: |kbar lo|_2 over the dims (bounds the lo products)
   size_t total;
 };
 

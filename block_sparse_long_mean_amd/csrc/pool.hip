@@ -207,6 +207,19 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
     ((uint16_t*)(means + ml.khi))[o] = hb;
     ((uint16_t*)(means + ml.klo))[o] = lb;
   }
+  // |lo|_2 over the block's 128 dims (waves 0 and 1 hold K's dims): scoring
+  // with hi alone is off from hi + lo by at most |q|_2 times this
+  __shared__ float lsq[2];
+  float la = 0.f;
+  if (which == 0) {
+    const float hv = bf16_bits_to_f32(f32_to_bf16_bits(mean));
+    const float lv = bf16_bits_to_f32(f32_to_bf16_bits(mean - hv));
+    la = lv * lv;
+  }
+  la = wave_sum(la);
+  if ((tid & 63) == 0 && tid < 128) lsq[tid >> 6] = la;
+  __syncthreads();
+  if (tid == 0) ((float*)(means + ml.kbnd))[gb * g.hkv + h] = sqrtf(lsq[0] + lsq[1]);
 }
 
 hipError_t launch_meta(const Geo& g, hipStream_t st) {

@@ -5,9 +5,13 @@
 // (one PackGQA query tile of 128 packed rows of one KV head).  The tile's Q
 // rows are staged once in LDS; every wave takes 32-block column tiles of the
 // pooled keys and computes the 128x32 logit tile with bf16 MFMAs.  kbar is
-// fp32, split into bf16 hi + lo (two MFMAs per step, ~16 significant bits)
-// so that the normalised energies are accurate to ~1e-5 relative; fp32
-// queries are split the same way (three MFMAs).  Each lane owns one block
+// fp32, split into bf16 hi + lo (~16 significant bits, normalised energies
+// accurate to ~1e-5 relative).  The sweep multiplies by hi alone and bounds
+// what lo would add (Cauchy-Schwarz, per block); only the few blocks whose
+// keep/drop decision or claim to the maximum the bound leaves open are
+// scored again with hi + lo, so the kept set is that of hi + lo scoring.
+// With energies requested, and for fp32 queries (split the same way, three
+// MFMAs), every block is scored with hi + lo.  Each lane owns one block
 // column and 64 of its 128 rows, so the per-block maximum m_J and the energy
 // S_J = sum_r 2^(s_rJ log2 e - m_J) (the form of Eq. 1, in log2 units) need
 // only one cross-lane exchange and no workgroup barrier; the final rescale
@@ -20,7 +24,7 @@
 namespace fp {
 
 template <int DT>
-__global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml, const void* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 ? 2 : 3))) void score_select_kernel(Geo g, MeansLayout ml, const void* __restrict__ q,
                                                            const char* __restrict__ means, float alpha,
                                                            int sink, int win, int32_t* __restrict__ counts,
                                                            uint32_t* __restrict__ bits,
@@ -31,8 +35,10 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   uint16_t* ql = qh + kRows * kQPitch;
   float* mJ = (float*)(smem + NQ * kRows * kQPitch * 2);
   float* SJ = mJ + g.max_nj;
-  __shared__ float red[4];
-  __shared__ int nsel_w[4];
+  int* flg = (int*)(SJ + g.max_nj);  // blocks scored again with hi + lo
+  __shared__ float red[4], qred[4];
+  __shared__ int nsel_w[4], nflag_sh, nunc_sh;
+  __shared__ float pm[4][32], ps[4][32];  // per-wave partial statistics of re-scored blocks
 
   const int64_t s = blockIdx.x;
   const SegCoord c = seg_coord(g, s);
@@ -53,20 +59,34 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
   const bf16x8* kls = klo + ((jt0 * g.hkv + c.h) * 8) * 64;
   const int64_t jstride = (int64_t)g.hkv * 8 * 64;
   const int nrows = t.nrows;
-  auto kb_load = [&](int jt, bf16x8 (&bh)[8], bf16x8 (&bl)[8]) {
+  // B operand fragments (hi, and lo when EXACT) of column tile jt
+  auto kb_load = [&](auto exact_tag, int jt, bf16x8 (&bh)[8], bf16x8 (&bl)[8]) {
+    constexpr bool EXACT = decltype(exact_tag)::value;
     const bf16x8* ph = khs + jt * jstride;
     const bf16x8* pl = kls + jt * jstride;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       bh[ks] = ph[ks * 64 + lane];
-      bl[ks] = pl[ks * 64 + lane];
+      if constexpr (EXACT) bl[ks] = pl[ks * 64 + lane];
     }
   };
-  // logits of the 128 rows x 32 blocks of column tile jt, 32 rows at a time;
-  // per block (= lane column) the running maximum of the raw products (sl > 0)
-  // and the sum of 2^(logit - max), logits in log2 units
-  auto tile = [&](auto ragged_tag, int jt, const bf16x8 (&bh)[8], const bf16x8 (&bl)[8]) {
+  // hi and lo fragments of block J for this lane's column (a gathered tile)
+  auto kb_gather = [&](int J, bf16x8 (&bh)[8], bf16x8 (&bl)[8]) {
+    const int64_t o = (int64_t)(J >> 5) * jstride + (J & 31) + 32 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bh[ks] = khs[o + ks * 64];
+      bl[ks] = kls[o + ks * 64];
+    }
+  };
+  // logits of the 128 rows x 32 blocks whose operands are loaded (block J for
+  // this lane's column), 32 rows at a time; per block the running maximum of
+  // the raw products (sl > 0) and the sum of 2^(logit - max), logits in log2
+  // units; EXACT uses kbar = hi + lo, otherwise hi alone
+  auto tile = [&](auto ragged_tag, auto exact_tag, int J, bool store, const bf16x8 (&bh)[8],
+                  const bf16x8 (&bl)[8]) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
+    constexpr bool EXACT = decltype(exact_tag)::value;
     float m = -INFINITY, sum = 0.f;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -76,10 +96,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
       for (int ks = 0; ks < 8; ++ks) {
         bf16x8 a = *(const bf16x8*)(arow + ks * 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc, 0, 0, 0);
-        if constexpr (NQ == 2) {
-          bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc, 0, 0, 0);
+        if constexpr (EXACT) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc, 0, 0, 0);
+          if constexpr (NQ == 2) {
+            bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc, 0, 0, 0);
+          }
         }
       }
       // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4; padding
@@ -110,48 +132,200 @@ __global__ __launch_bounds__(256) void score_select_kernel(Geo g, MeansLayout ml
     const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(sum, 32, 64);
     const float mx = fmaxf(m, mo) * sl;
     sum = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -mx)) + so * __builtin_amdgcn_exp2f(fmaf(mo, sl, -mx));
-    const int J = jt * 32 + col;
-    if (half == 0 && J < nc) {
+    if (half == 0 && store) {
       mJ[J] = mx;
       SJ[J] = sum;
     }
   };
+  // Scoring with kbar's hi part alone, unless energies are wanted or the
+  // queries are fp32.  Its logits are off from the hi + lo ones by at most
+  // sl * max_r |q_r|_2 * |lo_J|_2 per block (Cauchy-Schwarz; d_J below), so a
+  // block's energy is known within a factor 2^(+-d_J); blocks whose keep/drop
+  // decision that interval leaves open, and the blocks that may hold the
+  // maximum, are scored again with hi + lo.  The kept set is the hi + lo
+  // kernel's.
+  const bool exact = NQ == 2 || energies != nullptr;
   // one register set of operands per wave; the first column tile's load is in
   // flight while Q is staged
   bf16x8 bh[8], bl[8];
-  if (wave < njt) kb_load(wave, bh, bl);
+  if (wave < njt) {
+    if (exact)
+      kb_load(std::true_type{}, wave, bh, bl);
+    else
+      kb_load(std::false_type{}, wave, bh, bl);
+  }
+  // |lo_J|_2 of this thread's first four blocks, loaded ahead of the sweep
+  const float* kbnd = (const float*)(means + ml.kbnd) + (int64_t)g.blk_base[c.b] * g.hkv + c.h;
+  float kb4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (!exact) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int J = threadIdx.x + 256 * k;
+      if (J < nc) kb4[k] = kbnd[(int64_t)J * g.hkv];
+    }
+  }
   stage_q<DT>(g, c, t, q, qh, ql);
   __syncthreads();
-  auto sweep = [&](auto ragged_tag) {
+  if (!exact) {
+    // max_r |q_r|^2 of the wave's 32 rows: the largest entry of their Gram
+    // matrix Q Q^T (off-diagonal entries are bounded by the diagonal ones);
+    // the A and B fragments of Q Q^T are the same registers
+    f32x16 gacc = f32x16{};
+    const uint16_t* arow = qh + (wave * 32 + col) * kQPitch + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a = *(const bf16x8*)(arow + ks * 16);
+      gacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, gacc, 0, 0, 0);
+    }
+    float gm = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) gm = fmaxf(gm, gacc[r]);
+    gm = wave_max(gm);
+    if (lane == 0) qred[wave] = gm;  // read after the sweep's barrier
+  }
+  auto sweep = [&](auto ragged_tag, auto exact_tag) {
     for (int jt = wave; jt < njt; jt += 4) {
-      if (jt != wave) kb_load(jt, bh, bl);
-      tile(ragged_tag, jt, bh, bl);
+      if (jt != wave) kb_load(exact_tag, jt, bh, bl);
+      tile(ragged_tag, exact_tag, jt * 32 + col, jt * 32 + col < nc, bh, bl);
     }
   };
-  if (nrows < kRows)
-    sweep(std::true_type{});
-  else
-    sweep(std::false_type{});
+  if (exact) {
+    if (nrows < kRows)
+      sweep(std::true_type{}, std::true_type{});
+    else
+      sweep(std::false_type{}, std::true_type{});
+  } else {
+    if (nrows < kRows)
+      sweep(std::true_type{}, std::false_type{});
+    else
+      sweep(std::false_type{}, std::false_type{});
+  }
   __syncthreads();
 
   // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced.
+  auto forced_block = [&](int J) { return J < sink || (J >= t.beta - win && J < t.beta) || J >= t.beta; };
   float lm = -INFINITY;
   for (int J = threadIdx.x; J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
   const float M = block_max(lm, red);
-  float le = 0.f;
-  for (int J = threadIdx.x; J < nc; J += 256) {
-    float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
-    SJ[J] = e;
-    le = fmaxf(le, e);
+  float Emax, thr;
+  if (exact) {
+    float le = 0.f;
+    for (int J = threadIdx.x; J < nc; J += 256) {
+      float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
+      SJ[J] = e;
+      le = fmaxf(le, e);
+    }
+    Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
+    thr = alpha * Emax;
+  } else {
+    // bounds: the hi + lo energy of block J lies in [E_J 2^-d_J, E_J 2^d_J]
+    auto each_block = [&](auto&& body) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int J = threadIdx.x + 256 * k;
+        if (J < nc) body(J, kb4[k]);
+      }
+      for (int J = threadIdx.x + 1024; J < nc; J += 256) body(J, kbnd[(int64_t)J * g.hkv]);
+    };
+    const float q2 = sqrtf(fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3])) * (1.f + 0.001f));
+    const float dsc = sl * q2 * (1.f + 0.0078125f);
+    float lhi = 0.f, llo = 0.f;
+    each_block([&](int J, float lb) {
+      const float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
+      const float d = dsc * lb;
+      SJ[J] = e;
+      lhi = fmaxf(lhi, e * __builtin_amdgcn_exp2f(d));
+      llo = fmaxf(llo, e * __builtin_amdgcn_exp2f(-d));
+    });
+    // max E lies in [elo, ehi]: one two-value workgroup maximum
+    lhi = wave_max(lhi);
+    llo = wave_max(llo);
+    if (lane == 0) {
+      pm[0][wave] = lhi;
+      pm[1][wave] = llo;
+    }
+    if (threadIdx.x == 0) nflag_sh = nunc_sh = 0;
+    __syncthreads();
+    const float ehi = fmaxf(fmaxf(pm[0][0], pm[0][1]), fmaxf(pm[0][2], pm[0][3]));
+    const float elo = fmaxf(fmaxf(pm[1][0], pm[1][1]), fmaxf(pm[1][2], pm[1][3]));
+    // decided blocks become +inf (kept) or 0 (dropped); the others, and every
+    // block that may hold the maximum, go to the list for hi + lo scoring
+    constexpr float kEps = 1e-4f;
+    each_block([&](int J, float lb) {
+      const float e = SJ[J], d = dsc * lb;
+      const float up = e * __builtin_amdgcn_exp2f(d) * (1.f + kEps), dn = e * __builtin_amdgcn_exp2f(-d);
+      const bool keep = dn >= alpha * ehi * (1.f + kEps), drop = up < alpha * elo;
+      const bool maxc = up >= elo;
+      const bool unc = !forced_block(J) && !keep && !drop;
+      if (unc) atomicAdd(&nunc_sh, 1);
+      if (unc || maxc) flg[atomicAdd(&nflag_sh, 1)] = J;
+      SJ[J] = keep ? INFINITY : (drop ? 0.f : e);
+    });
+    __syncthreads();
+    // nothing undecided: the bounds alone give the kept set
+    const int nflag = nunc_sh > 0 ? nflag_sh : 0;
+    // hi + lo scoring of the listed blocks, 32 at a time, wave w taking rows
+    // 32w..32w+31; the four partial (max, sum) pairs are merged per block
+    for (int g0 = 0; g0 < nflag; g0 += 32) {
+      const int J = flg[min(g0 + col, nflag - 1)];
+      kb_gather(J, bh, bl);
+      f32x16 acc = f32x16{};
+      const uint16_t* arow = qh + (wave * 32 + col) * kQPitch + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(arow + ks * 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) acc[r] = -INFINITY;
+      float m = acc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, acc[r]);
+      const float mo = fmaxf(m, __shfl_xor(m, 32, 64));  // the wave's 32 rows of the block
+      const float msl = mo == -INFINITY ? 0.f : mo * sl;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], sl, -msl));
+      sum += __shfl_xor(sum, 32, 64);
+      if (half == 0) {
+        pm[wave][col] = mo;
+        ps[wave][col] = sum;
+      }
+      __syncthreads();
+      if (wave == 0 && half == 0 && g0 + col < nflag) {
+        const float mx = fmaxf(fmaxf(pm[0][col], pm[1][col]), fmaxf(pm[2][col], pm[3][col])) * sl;
+        float st = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) st += ps[w][col] * __builtin_amdgcn_exp2f(fmaf(pm[w][col], sl, -mx));
+        mJ[J] = mx;
+        SJ[J] = st;
+      }
+      __syncthreads();
+    }
+    // hi + lo energies of the listed blocks; the maximum is among them.
+    // Decided blocks hold +inf (kept) or 0 (dropped): with none re-scored the
+    // threshold only has to separate those two
+    Emax = 0.f;
+    thr = INFINITY;
+    if (nflag > 0) {
+      float le = 0.f;
+      for (int i = threadIdx.x; i < nflag; i += 256) {
+        const int J = flg[i];
+        const float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
+        SJ[J] = e;
+        le = fmaxf(le, e);
+      }
+      Emax = block_max(le, red);
+      thr = alpha * Emax;
+    }
   }
-  const float Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
-  const float thr = alpha * Emax;
   int nsel = 0;
   for (int base = wave * 64; base < nc; base += 256) {
     const int J = base + lane;
     const bool in = J < nc;
-    const bool forced = J < sink || (J >= t.beta - win && J < t.beta) || J >= t.beta;
-    const bool sel = in && (forced || SJ[J] >= thr);
+    const bool sel = in && (forced_block(J) || SJ[J] >= thr);
     const uint64_t m = __ballot(sel);
     if (lane == 0) {
       int w0 = base >> 5;
@@ -256,7 +430,9 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
                                float alpha, int sink, int win, int32_t* counts, uint32_t* bits,
                                float* energies, hipStream_t st) {
   const int nq = g.dtype == kF32 ? 2 : 1;
-  size_t lds = (size_t)nq * kRows * kQPitch * 2 + (size_t)g.max_nj * 8;
+  // per block: m_J and S_J, and (bf16 / e4m3: hi-only scoring) the re-score list
+  const int per_blk = nq == 2 ? 8 : 12;
+  size_t lds = (size_t)nq * kRows * kQPitch * 2 + (size_t)g.max_nj * per_blk;
   dim3 grid((unsigned)g.n_seg);
   static bool attr_set[3] = {false, false, false};
   if (!attr_set[g.dtype]) {
@@ -264,7 +440,7 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
                      : g.dtype == kF32 ? (const void*)score_select_kernel<kF32>
                                        : (const void*)score_select_kernel<kE4M3>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       2 * kRows * kQPitch * 2 + kMaxBlocks * 8);
+                                       nq * kRows * kQPitch * 2 + kMaxBlocks * per_blk);
     if (e != hipSuccess) return e;
     attr_set[g.dtype] = true;
   }
