@@ -1,0 +1,56 @@
+"""The index stage scores most blocks with the bf16 hi part of the pooled keys
+alone and re-scores with hi + lo only the blocks that its bound on the missing
+lo term leaves undecided (and the possible maxima).  Requesting the energies
+switches every block to hi + lo scoring.  The two must produce the same CSR on
+every segment: these tests run both on whole workloads (no oracle involved; the
+CSR parity against the oracle is in test_gpu_parity.py and the workload tests).
+"""
+import numpy as np
+import pytest
+
+from block_sparse_long_mean_amd import configs, synth
+from tests.gpu_harness import GpuRun
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(run):
+    cu_f, idx_f = run.select()
+    cu_e, idx_e, _ = run.select(energies=True)
+    return cu_f, idx_f, cu_e, idx_e
+
+
+@pytest.mark.parametrize("name,alpha,sink,win", [
+    ("qwen3_30b_a3b_32k_bf16", 0.1, 2, 4),
+    ("qwen3_30b_a3b_32k_bf16", 0.2, 1, 1),
+    ("qwen3_30b_a3b_128k_e4m3", 0.1, 2, 4),
+    ("chunk_mix_paged_bf16", 0.1, 2, 4),
+    ("paged_varlen_16req_bf16", 0.1, 2, 4),
+])
+def test_bounded_scoring_keeps_the_exact_set(name, alpha, sink, win):
+    w = configs.ALL[name]
+    print(f"[case] bounded vs exact scoring {name} alpha={alpha}", flush=True)
+    b, pg = w.make()
+    run = GpuRun(b, paged=pg, alpha=alpha, sink=sink, win=win)
+    cu_f, idx_f, cu_e, idx_e = _both(run)
+    nseg = len(cu_f) - 1
+    same = np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e)
+    if not same:
+        diff = [s for s in range(nseg)
+                if not np.array_equal(idx_f[cu_f[s]:cu_f[s + 1]], idx_e[cu_e[s]:cu_e[s + 1]])]
+        raise AssertionError(f"{len(diff)} of {nseg} segments differ, first {diff[:5]}")
+    print(f"  {nseg} segments, {len(idx_f)} entries: identical", flush=True)
+    assert run.device_error() == 0
+
+
+def test_bounded_scoring_extremes():
+    """Ragged and single-row tiles, alpha 0 (everything kept) and alpha 1 (only
+    blocks tied with the maximum), keys with a wide dynamic range."""
+    b = synth.make_batch([1, 130, 2500, 7000], 32, 4, 128, seed=53, dtype="bf16", clusters=True,
+                         diag_bias=True)
+    for alpha in (0.0, 1.0, 0.5):
+        print(f"[case] extremes alpha={alpha}", flush=True)
+        run = GpuRun(b, alpha=alpha, sink=1, win=1)
+        cu_f, idx_f, cu_e, idx_e = _both(run)
+        assert np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e)
+        assert run.device_error() == 0
