@@ -144,7 +144,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
   // decision that interval leaves open, and the blocks that may hold the
   // maximum, are scored again with hi + lo.  The kept set is the hi + lo
   // kernel's.
-  const bool exact = NQ == 2 || energies != nullptr;
+  // (also for tiles with at most two column tiles, where the bound's fixed
+  // cost outweighs the halved sweep)
+  const bool exact = NQ == 2 || energies != nullptr || njt <= 2;
   // one register set of operands per wave; the first column tile's load is in
   // flight while Q is staged
   bf16x8 bh[8], bl[8];
