@@ -155,6 +155,19 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
 #define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
+// x of this lane and of lane ^ 32 (the lane in the other half that holds
+// the same query row), by one v_permlane32_swap instead of an LDS permute.
+__device__ __forceinline__ float2 with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // r[0]: lanes 0-31 keep their x, lanes 32-63 get x of lane - 32; r[1]: lanes
+  // 0-31 get x of lane + 32, lanes 32-63 keep theirs
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const float2 p = with_other_half(x);
+  return fmaxf(p.x, p.y);
+}
+
 // An empty use of a register value: it must be computed before this point.
 template <typename V>
 __device__ __forceinline__ void pin(const V& x) {
@@ -716,7 +729,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               float mh = sv[0];
 #pragma unroll
               for (int r = 1; r < 16; ++r) mh = fmaxf(mh, sv[r]);
-              mh = fmaxf(mh, __shfl_xor(mh, 32, 64));  // the other lane half holds the same query row
+              mh = max_halves(mh);  // the other lane half holds the same query row
               const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
               const float m_new = fmaxf(m_i, m_half);
               const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -1162,7 +1175,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           a = fmaxf(a, fmaxf(sacc[0][15], b));
           mx = fmaxf(sacc[1][15], a);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_halves(mx);
         // tile steps hold raw dot products (sl > 0); chunk steps are already scaled
         const float m_step = KIND == 2 ? mx : mx * sl;
         if (fresh) {
@@ -1294,7 +1307,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           float mh = fmaxf(a, sv[15]);
           {
             // the other lane half holds the same query row
-            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
+            mh = max_halves(mh);
           }
           const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
           const bool need = __any(m_half > m_i + kTau);
@@ -1356,7 +1369,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     if (err) atomicOr(&g.hdr->err, (int)err);
     if (tid == 0) sh_unit = ticket < own_hi - own_lo ? own_hi - 1 - ticket : steal(xcd + 1);
     const bool bad = __syncthreads_or(err != 0) != 0;
-    const float l_tot = l_i + __shfl_xor(l_i, 32, 64);
+    const float2 lp = with_other_half(l_i);
+    const float l_tot = lp.x + lp.y;
     if (DT == kBF16 && un.nsplit == 1 && !bad) {
       // bf16: the wave's 32 output rows pass through LDS (the K buffers, which
       // nothing reads after the unit's last barrier; rows padded to 272 bytes
