@@ -1211,8 +1211,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int jt = w >> 2, r = (w & 3) * 4;
-            const uint32_t word = f32x2_to_e4m3x2(sacc[jt][r], sacc[jt][r + 1]) |
-                                  (f32x2_to_e4m3x2(sacc[jt][r + 2], sacc[jt][r + 3]) << 16);
+            const uint32_t word = f32x4_to_e4m3x4(sacc[jt][r], sacc[jt][r + 1], sacc[jt][r + 2], sacc[jt][r + 3]);
             b[w] = (int)word;
           }
           if constexpr (VC) {

@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t f32x2_to_e4m3x2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 
+// Four floats -> four OCP E4M3 codes in one dword (a, b in the low half, c, d
+// in the high half), two conversions that each write one half of the word.
+// The first one's other half is a placeholder that the second overwrites.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // Four E4M3 codes (one dword) -> four floats.
 __device__ __forceinline__ f32x4 e4m3x4_to_f32(uint32_t w) {
   f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
