@@ -137,15 +137,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
       SJ[J] = sum;
     }
   };
-  // Scoring with kbar's hi part alone, unless energies are wanted or the
-  // queries are fp32.  Its logits are off from the hi + lo ones by at most
-  // sl * max_r |q_r|_2 * |lo_J|_2 per block (Cauchy-Schwarz; d_J below), so a
-  // block's energy is known within a factor 2^(+-d_J); blocks whose keep/drop
-  // decision that interval leaves open, and the blocks that may hold the
-  // maximum, are scored again with hi + lo.  The kept set is the hi + lo
-  // kernel's.
-  // (also for tiles with at most two column tiles, where the bound's fixed
-  // cost outweighs the halved sweep)
+  // The sweep multiplies by kbar's hi part alone.  Its logits are off from
+  // the hi + lo ones by at most sl * max_r |q_r|_2 * |lo_J|_2 per block
+  // (Cauchy-Schwarz; d_J below), so a block's energy is known within a factor
+  // 2^(+-d_J); blocks whose keep/drop decision that interval leaves open, and
+  // the blocks that may hold the maximum, are scored again with hi + lo.  The
+  // kept set is that of hi + lo scoring.  Every block is scored with hi + lo
+  // when energies are wanted, for fp32 queries, and for tiles with at most
+  // two column tiles (where the bound's fixed cost outweighs the halved sweep).
   const bool exact = NQ == 2 || energies != nullptr || njt <= 2;
   // one register set of operands per wave; the first column tile's load is in
   // flight while Q is staged
