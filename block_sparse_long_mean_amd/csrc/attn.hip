@@ -16,14 +16,16 @@
 // computed transposed, S^T = K Q^T (A = K tile from LDS, B = the wave's Q rows
 // held in registers), so each lane owns one query row: row max and row sum
 // are in-lane plus one exchange with lane^32, and the probabilities land in
-// exactly the register layout of the B operand of O^T += V^T P^T.  V is
-// therefore staged in LDS transposed, with its key order permuted to match
-// that register layout.  K/V tiles are gathered through the page table
-// ([V2] Eq. 22) with 8-element vector loads into registers one step ahead of
-// the MFMAs and written to the other half of a double-buffered LDS stage.
-// The persistent grid takes its work units from a list that the scheduler
-// cuts into work-balanced ranges, one per XCD, each served through an atomic
-// counter of its own.  bf16: v_mfma_f32_32x32x16_bf16; e4m3:
+// exactly the register layout of the B operand of O^T += V^T P^T.  K and V
+// tiles travel HBM -> LDS by buffer DMA (bf16, e4m3; through the page table,
+// [V2] Eq. 22, per tile or per row) into double-buffered LDS, one or two
+// steps ahead; V^T operands are read with the LDS transpose loads (or, for a
+// V stored transposed, directly).  fp32 stages K/V through registers.  bf16
+// runs a software pipeline across steps (the softmax of one step in pieces
+// between the MFMAs of its neighbours); e4m3 and fp32 take one step at a
+// time.  The persistent grid takes its work units from a list that the
+// scheduler cuts into work-balanced ranges, one per XCD, each served through
+// an atomic counter of its own.  bf16: v_mfma_f32_32x32x16_bf16; e4m3:
 // v_mfma_scale_f32_32x32x64_f8f6f4 with P quantised as e4m3(2^8 e^{s-m})
 // ([V2] Eq. 15); fp32: v_mfma_f32_32x32x2f32.
 #include "device_common.h"
