@@ -161,7 +161,10 @@ fp_status fp_pool(const fp_problem* prob, const void* k, const void* v, void* me
  * 2J+1 (a tile starting after the tile's last query position is dropped).
  * energies (optional, may be NULL): [n_segments][max_blocks] floats receive
  * E_J / max E for the candidate blocks J <= beta1 (the block of the segment's
- * last position) and -1 beyond.  idx_capacity is the int32 size of
+ * last position) and -1 beyond.  With energies requested every block is
+ * scored at full precision; without, most blocks are scored at reduced
+ * precision under an error bound and only those the bound leaves undecided are
+ * scored again, which yields the same cu/idx.  idx_capacity is the int32 size of
  * idx and must be >= fp_sizes.idx_capacity. */
 fp_status fp_select(const fp_problem* prob, const fp_select_params* params, const void* q,
                     const void* k, const void* v, int32_t* cu, int32_t* idx,
