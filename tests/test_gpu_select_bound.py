@@ -55,3 +55,29 @@ def test_bounded_scoring_extremes():
         cu_f, idx_f, cu_e, idx_e = _both(run)
         assert np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e)
         assert run.device_error() == 0
+
+
+def test_random_configurations():
+    """Seeded random batches (lengths, head counts, chunk offsets, alpha,
+    forced-block counts, bf16 / E4M3): bounded scoring must give the CSR of
+    hi + lo scoring of every block, segment for segment."""
+    rng = np.random.default_rng(2024)
+    for case in range(12):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(1, 4))
+        lengths = [int(x) for x in rng.integers(8000, 24000, size=n)]
+        qlens = [int(rng.integers(1, L + 1)) if rng.random() < 0.4 else L for L in lengths]
+        alpha = float(rng.choice([0.02, 0.1, 0.3, 0.7]))
+        sink, win = int(rng.integers(0, 3)), int(rng.integers(0, 5))
+        dtype = "e4m3" if rng.random() < 0.3 else "bf16"
+        print(f"[case] random {case}: lengths={lengths} q={qlens} hkv={hkv} g={g} alpha={alpha} "
+              f"sink={sink} win={win} {dtype}", flush=True)
+        b = synth.make_batch(lengths, hkv * g, hkv, 128, seed=100 + case, dtype="bf16", clusters=True,
+                             diag_bias=bool(rng.random() < 0.7), q_lengths=qlens)
+        if dtype == "e4m3":
+            b = synth.to_e4m3(b)
+        run = GpuRun(b, alpha=alpha, sink=sink, win=win)
+        cu_f, idx_f, cu_e, idx_e = _both(run)
+        assert np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e), case
+        assert run.device_error() == 0
