@@ -81,3 +81,18 @@ def test_random_configurations():
         cu_f, idx_f, cu_e, idx_e = _both(run)
         assert np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e), case
         assert run.device_error() == 0
+
+
+@pytest.mark.parametrize("qscale,kscale", [(8.0, 4.0), (0.125, 0.25)])
+def test_bounded_scoring_large_and_small_logits(qscale, kscale):
+    """Logits scaled up 32x (energies concentrated on few blocks, a wide bound
+    that leaves many blocks to re-score) and down 32x (nearly flat energies):
+    the CSR still equals that of hi + lo scoring of every block."""
+    print(f"[case] scaled logits q x{qscale} k x{kscale}", flush=True)
+    b = synth.make_batch([20000, 9000], 16, 2, 128, seed=61, dtype="bf16", clusters=True, diag_bias=True)
+    b.q = (b.q.float() * qscale).to(b.q.dtype)  # powers of two: exact in bf16
+    b.k = (b.k.float() * kscale).to(b.k.dtype)
+    run = GpuRun(b, alpha=0.1, sink=2, win=4)
+    cu_f, idx_f, cu_e, idx_e = _both(run)
+    assert np.array_equal(cu_f, cu_e) and np.array_equal(idx_f, idx_e)
+    assert run.device_error() == 0
