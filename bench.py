@@ -386,7 +386,7 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "copies": 5}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the operator runs on one GPU (sharding across GPUs is a design note, not code); --gpus must be 1"}))
         sys.exit(2)
     if args.sweep:
         sweep(args)
