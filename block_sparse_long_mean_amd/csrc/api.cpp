@@ -9,13 +9,32 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <set>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/fp.h"
 #include "fp_internal.h"
 
 using namespace fp;
+
+namespace fp {
+
+hipError_t set_lds_limit(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;  // (kernel, device) pairs already raised
+  std::lock_guard<std::mutex> lk(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
+
+}  // namespace fp
 
 namespace {
 
@@ -36,6 +55,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Host view of the batch, derived from the host copies of the offsets.
 struct HostGeo {
   int64_t total = 0, total_kv = 0, n_seg = 0, nb_pad = 0, idx_cap = 0;
+  int64_t step_cap = 0;  // most attention steps the scheduler can count (int32 prefix sums)
   int32_t max_len = 0, max_nj = 1, words = 1, g = 1, log2g = 0;  // max_len: longest K/V sequence
 };
 
@@ -87,11 +107,16 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
     hg->n_seg += (int64_t)p->num_heads_kv * nt;
     const int64_t nj = (L + kBlock - 1) / kBlock;
     hg->nb_pad += (nj + kChunk - 1) / kChunk * kChunk;
-    // worst-case CSR: every causal tile of every segment
+    // worst-case CSR: every causal tile of every segment; worst-case step count
+    // of the scheduler: a listed count clamped to both tiles of every candidate
+    // block, plus every correction chunk
     for (int64_t I = 0; I < nt; ++I) {
+      int64_t r0 = I * kRows;
       int64_t r1 = std::min((I + 1) * kRows, Lq << hg->log2g);
+      int64_t t0 = off + (r0 >> hg->log2g);
       int64_t t1 = off + ((r1 - 1) >> hg->log2g);
       hg->idx_cap += (int64_t)p->num_heads_kv * (t1 / kTile + 1);
+      hg->step_cap += (int64_t)p->num_heads_kv * (2 * (t1 / kBlock + 1) + (t0 / kBlock + kChunk - 1) / kChunk);
     }
   }
   hg->total = cu[p->num_reqs];
@@ -99,6 +124,9 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
   if (hg->total > INT32_MAX / 2) return fail(FP_ERR_UNSUPPORTED, "total_q too large");
   if (hg->n_seg > INT32_MAX / 16 || hg->idx_cap > INT32_MAX)
     return fail(FP_ERR_UNSUPPORTED, "too many segments for int32 CSR offsets");
+  if (hg->step_cap > INT32_MAX)
+    return fail(FP_ERR_UNSUPPORTED, "up to %lld attention steps: too many for the scheduler's int32 sums",
+                (long long)hg->step_cap);
   hg->max_len = (int32_t)max_len;
   hg->max_nj = (int32_t)std::max<int64_t>(1, (max_len + kBlock - 1) / kBlock);
   hg->words = (hg->max_nj + 31) / 32 + 1;
@@ -157,6 +185,7 @@ MeansLayout means_layout(const fp_problem* p, const HostGeo& hg) {
   m.klo = o; o = align256(o + rows * 2);
   m.kop = o; o = align256(o + rows * elem_size(p->dtype));
   m.vop = o; o = align256(o + rows * elem_size(p->dtype));
+  m.klo8 = o; o = align256(o + (p->dtype == FP_E4M3 ? rows : 0));
   m.kbnd = o; o = align256(o + (size_t)hg.nb_pad * p->num_heads_kv * 4);
   m.total = o;
   return m;
@@ -191,7 +220,9 @@ SplitPolicy split_policy(const fp_problem* p, const HostGeo& hg) {
   return sp;
 }
 
-WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp) {
+// with_select: the selection bitmasks of fp_select (the attention calls never
+// touch them, so a layout for attention alone leaves them out).
+WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp, bool with_select = true) {
   WsLayout w{};
   size_t o = 0;
   w.umax = sp.umax;
@@ -200,7 +231,7 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
   w.blk_base = o; o = align256(o + (size_t)(p->num_reqs + 1) * 4);
   w.counts = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.scan_part = o; o = align256(o + (size_t)((hg.n_seg + 1023) / 1024 + 1) * 4);
-  w.bits = o; o = align256(o + (size_t)hg.n_seg * hg.words * 4);
+  w.bits = o; o = align256(o + (with_select ? (size_t)hg.n_seg * hg.words * 4 : 0));
   w.work = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.wscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
   w.uscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
@@ -350,14 +381,12 @@ fp_status fp_select(const fp_problem* prob, const fp_select_params* params, cons
   return FP_OK;
 }
 
-static fp_status run_attn(const fp_problem* prob, const void* q, const void* k, const void* v, const int32_t* cu,
-                          const int32_t* idx, const void* means, int dense, int correction, void* out,
-                          float* lse, void* ws, size_t ws_bytes, void* stream) {
-  Prepared pr;
-  fp_status s = prepare(prob, ws, ws_bytes, &pr);
-  if (s != FP_OK) return s;
-  if (!q || !k || !v || !out) return fail(FP_ERR_INVALID_ARG, "q, k, v and out are required");
-  if (!dense && (!cu || !idx || !means)) return fail(FP_ERR_INVALID_ARG, "cu, idx and means are required");
+// The attention launch sequence on a prepared problem.  Every workspace word
+// it reads is written earlier in the same sequence (metadata, scheduler sums,
+// counters, unit list), so the workspace needs no clearing between calls.
+static fp_status launch_attention(const fp_problem* prob, Prepared& pr, const void* q, const void* k, const void* v,
+                                  const int32_t* cu, const int32_t* idx, const void* means, int dense,
+                                  int correction, void* out, float* lse, void* ws, void* stream) {
   if (pr.hg.total == 0) return FP_OK;
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
@@ -369,6 +398,18 @@ static fp_status run_attn(const fp_problem* prob, const void* q, const void* k, 
   if (pr.sp.umax > 1) FP_LAUNCH(launch_combine(pr.g, pr.wl, wsb, out, lse, st));
   return FP_OK;
 }
+
+static fp_status run_attn(const fp_problem* prob, const void* q, const void* k, const void* v, const int32_t* cu,
+                          const int32_t* idx, const void* means, int dense, int correction, void* out,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Prepared pr;
+  fp_status s = prepare(prob, ws, ws_bytes, &pr);
+  if (s != FP_OK) return s;
+  if (!q || !k || !v || !out) return fail(FP_ERR_INVALID_ARG, "q, k, v and out are required");
+  if (!dense && (!cu || !idx || !means)) return fail(FP_ERR_INVALID_ARG, "cu, idx and means are required");
+  return launch_attention(prob, pr, q, k, v, cu, idx, means, dense, correction, out, lse, ws, stream);
+}
+
 
 fp_status fp_sparse_attn(const fp_problem* prob, const fp_select_params* params, const void* q, const void* k,
                          const void* v, const int32_t* cu, const int32_t* idx, const void* means,

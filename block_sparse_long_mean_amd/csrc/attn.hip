@@ -69,6 +69,12 @@ __device__ __forceinline__ typename Tr<DT>::Op lds_op(const char* p) {
   }
 }
 
+// e4m3 with the A operand scaled by 2^-4 (E8M0 exponent 123): the lo part of
+// the pooled keys, stored 16 times larger than it stands for
+__device__ __forceinline__ f32x16 mma_lo8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 123, 0, 127);
+}
+
 template <int DT>
 __device__ __forceinline__ f32x16 mma(typename Tr<DT>::Op a, typename Tr<DT>::Op b, f32x16 c) {
   if constexpr (DT == kBF16)
@@ -111,7 +117,9 @@ struct Cfg {
   static constexpr int KBYTES = kTile * KPITCH;
   static constexpr int VBYTES = DMA ? kTile * VPITCH : kD * VPITCH;
   static constexpr int PENBYTES = 2 * 32 * 4;    // correction-step logit offsets, per lane half
-  static constexpr int STAGE = KBYTES + VBYTES + PENBYTES;
+  // e4m3: the lo part of the pooled keys of a correction step (k rows again)
+  static constexpr int LOOFF = KBYTES + VBYTES + PENBYTES;
+  static constexpr int STAGE = LOOFF + (DT == kE4M3 ? KBYTES : 0);
   static constexpr int SELOFF = DT == kBF16 ? PipeL::SEL : 2 * STAGE;  // selection bitmask of the unit
   static constexpr int LDS = DT == kBF16 ? PipeL::LDS : 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
   static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
@@ -432,6 +440,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const uint64_t mbase = ((uint64_t)ur.blk_base * g.hkv + c.h) * kD * EB;
     const char* kmbase = means + ml.kop + mbase;
     const char* vmbase = means + ml.vop + mbase;
+    const char* klmbase = means + ml.klo8 + mbase;  // e4m3 only
     // transposed V (e4m3): this head's dim rows, and the transposed correction
     // operands ([chunk][head][dim][64 blocks]) of the request's first chunk
     const char* vtbase = (const char*)v + (AM == kContig ? (uint64_t)c.h * kD * g.vrow + c.kv0 : 0);
@@ -1033,6 +1042,13 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             bld8<DT>(vst[i], rv, voff_v[i], 0);
           }
         }
+        if constexpr (DT == kE4M3) {
+          // the pooled keys' lo part, staged like the keys
+          const __amdgpu_buffer_rsrc_t rl = make_rsrc(klmbase + o, left);
+          char* ls = smem + buf * C::STAGE + C::LOOFF;
+#pragma unroll
+          for (int qq = 0; qq < C::NDMA; ++qq) dma16(rl, ls + (16 * wave + C::RPI * qq) * C::ROWB, dk[qq]);
+        }
       }
       if constexpr (C::DMA) write_pen(buf, it);
     };
@@ -1141,6 +1157,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         sacc[jt] = f32x16{};
 #pragma unroll
         for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma<DT>(k_op(ks, jt, m), qf[m], sacc[jt]);
+        if constexpr (DT == kE4M3 && KIND == 2) {
+          // pooled keys = hi + 2^-4 lo: the lo products accumulate into the same logits
+#pragma unroll
+          for (int m = 0; m < C::NM0; ++m) sacc[jt] = mma_lo8(k_op(ks + C::LOOFF, jt, m), qf[m], sacc[jt]);
+        }
       }
       if constexpr (DT == kE4M3) {
         // key j of this lane's register r of logit tile jt: 32 jt + 8 (r/4) + 4 half + r%4
@@ -1533,13 +1554,8 @@ static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, cons
                                 const void* q, const void* k, const void* v, const int32_t* cu,
                                 const int32_t* idx, const char* means, int correction, void* out,
                                 float* lse, int grid, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<DT, DENSE, AM, VC>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<DT>::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit((const void*)attn_kernel<DT, DENSE, AM, VC>, Cfg<DT>::LDS);
+  if (e != hipSuccess) return e;
   attn_kernel<DT, DENSE, AM, VC><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
                                                                       correction, out, lse);
   return hipGetLastError();

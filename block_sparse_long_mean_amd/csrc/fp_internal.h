@@ -65,6 +65,7 @@ struct MeansLayout {
   size_t kbar32, vbar32;  // float [nb_pad][hkv][128]
   size_t khi, klo;        // bf16, MFMA B-operand order: [nb_pad/32][hkv][8][64][8]
   size_t kop, vop;        // element dtype, [nb_pad][hkv][128]: operands of correction steps
+  size_t klo8;            // E4M3 only, [nb_pad][hkv][128]: kbar/c_k - kop, times 16, as E4M3
   size_t kbnd;            // float [nb_pad][hkv]: |kbar lo|_2 over the dims (bounds the lo products)
   size_t total;
 };
@@ -116,5 +117,9 @@ hipError_t launch_combine(const Geo& g, const WsLayout& wl, char* ws, void* out,
                           hipStream_t st);
 
 int attn_wgs_per_cu(int dtype);
+
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once per
+// (kernel, device); safe to call from several host threads.
+hipError_t set_lds_limit(const void* fn, int bytes);
 
 }  // namespace fp

@@ -213,15 +213,12 @@ hipError_t launch_block_mass(const Geo& g, const MeansLayout& ml, const void* q,
   const int nq = g.dtype == kF32 ? 2 : 1;
   const size_t lds = (size_t)nq * kRows * kQPitch * 2 + kRows * 8;
   dim3 grid((unsigned)g.n_seg);
-  static bool attr_set[3] = {false, false, false};
-  if (!attr_set[g.dtype]) {
+  {
     const void* fn = g.dtype == kBF16 ? (const void*)block_mass_kernel<kBF16>
                      : g.dtype == kF32 ? (const void*)block_mass_kernel<kF32>
                                        : (const void*)block_mass_kernel<kE4M3>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       2 * kRows * kQPitch * 2 + kRows * 8);
+    hipError_t e = set_lds_limit(fn, 2 * kRows * kQPitch * 2 + kRows * 8);
     if (e != hipSuccess) return e;
-    attr_set[g.dtype] = true;
   }
   switch (g.dtype) {
     case kBF16:

@@ -193,7 +193,17 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
   } else {
     // transposed V: the correction operands of a 64-block chunk are [dim][block]
     const int64_t el = which && vcols ? (((gb >> 6) * g.hkv + h) * kD + d) * kChunk + (gb & 63) : row_el;
-    ((uint8_t*)op)[el] = (uint8_t)f32x2_to_e4m3x2(mean / (which ? cv : ck), 0.f);
+    const float x = fminf(448.f, fmaxf(-448.f, mean / (which ? cv : ck)));
+    const uint32_t hi = f32x2_to_e4m3x2(x, 0.f);
+    ((uint8_t*)op)[el] = (uint8_t)hi;
+    if (which == 0) {
+      // kbar/c_k = hi + lo/16: the part that the E4M3 code drops, scaled by 2^4
+      // and rounded again, so that the correction logits carry ~8 significant
+      // bits (the attention kernel multiplies lo back by 2^-4 through the MFMA's
+      // operand scale)
+      const float r = (x - e4m3x4_to_f32(hi)[0]) * 16.f;
+      ((uint8_t*)(means + ml.klo8))[row_el] = (uint8_t)f32x2_to_e4m3x2(fminf(448.f, fmaxf(-448.f, r)), 0.f);
+    }
   }
   if (which == 0) {
     // kbar = hi + lo in bf16, stored in MFMA B-operand order:

@@ -435,15 +435,12 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
   const int per_blk = nq == 2 ? 8 : 12;
   size_t lds = (size_t)nq * kRows * kQPitch * 2 + (size_t)g.max_nj * per_blk;
   dim3 grid((unsigned)g.n_seg);
-  static bool attr_set[3] = {false, false, false};
-  if (!attr_set[g.dtype]) {
+  {
     const void* fn = g.dtype == kBF16 ? (const void*)score_select_kernel<kBF16>
                      : g.dtype == kF32 ? (const void*)score_select_kernel<kF32>
                                        : (const void*)score_select_kernel<kE4M3>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       nq * kRows * kQPitch * 2 + kMaxBlocks * per_blk);
+    hipError_t e = set_lds_limit(fn, nq * kRows * kQPitch * 2 + kMaxBlocks * per_blk);
     if (e != hipSuccess) return e;
-    attr_set[g.dtype] = true;
   }
   switch (g.dtype) {
     case kBF16:

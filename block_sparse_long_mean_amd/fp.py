@@ -76,7 +76,7 @@ _lib.fp_status_string.argtypes = [C.c_int]
 _lib.fp_last_error.restype = C.c_char_p
 _lib.fp_last_error.argtypes = []
 
-EXPORTS = ["fp_query_sizes", "fp_pool", "fp_select", "fp_sparse_attn", "fp_dense_attn",
+EXPORTS = ["fp_query_sizes", "fp_pool", "fp_select", "fp_sparse_attn", "fp_dense_attn", "fp_block_mass",
            "fp_read_device_error", "fp_block_base", "fp_status_string", "fp_last_error"]
 
 

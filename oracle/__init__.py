@@ -96,6 +96,12 @@ def lib():
         L.fpo_attend_list.restype = None
         L.fpo_attend_list.argtypes = [P, dp, dp, C.c_int64, i64p, i32p, i32p, C.c_int, C.c_int,
                                       C.c_int, dp, dp]
+        L.fpo_attend_tile_eq15.restype = None
+        L.fpo_attend_tile_eq15.argtypes = [P, dp, dp, C.c_int, C.c_int, C.c_int64, i32p, C.c_int64,
+                                           C.c_int, C.c_int, C.c_int, C.c_double, dp, dp, dp, dp]
+        L.fpo_attend_list_eq15.restype = None
+        L.fpo_attend_list_eq15.argtypes = [P, dp, dp, C.c_int64, i64p, i32p, i32p, C.c_int, C.c_int,
+                                           i32p, C.c_double, dp, dp, dp, dp]
         L.fpo_block_mass_tile.restype = C.c_int64
         L.fpo_block_mass_tile.argtypes = [P, dp, C.c_int, C.c_int, C.c_int64, dp, dp]
         L.fpo_block_mass_list.restype = None
@@ -298,6 +304,55 @@ class Problem:
             C.byref(self._s), _ptr(kb, C.c_double), _ptr(vb, C.c_double), n, _ptr(segs, C.c_int64),
             _ptr(cu_a, C.c_int32), _ptr(idx_a, C.c_int32), 1 if dense else 0,
             1 if correction else 0, 1 if p8 else 0, _ptr(out, C.c_double), _ptr(lse, C.c_double))
+        return out, lse
+
+    def attend_segments_eq15(self, segs, cu, idx, correction=True, rounding=True, nsplit=None, logit_err=0.0):
+        """[V2] Eq. 15 as printed (E4M3 weights rounded against the running row
+        maximum, steps in Eq. 17 order then the correction chunks; ``nsplit``: the
+        KV split count of each listed segment, None = 1): (out [n,R,d], lse [n,R]).
+        ``rounding=False`` runs the same recurrence unrounded.  With ``logit_err`` > 0
+        also returns (allow [n,R], lallow [n,R]): how far each row's output (max-abs)
+        and LSE can move if every weight whose rounding an implementation with logits
+        off by up to logit_err * sigma * sum|q_i k_i| could flip took its other
+        rounding."""
+        kb, vb = self.pool()
+        segs = np.ascontiguousarray(np.asarray(segs, np.int64))
+        n = len(segs)
+        out = np.zeros((n, self.rows, self.d), np.float64)
+        lse = np.zeros((n, self.rows), np.float64)
+        cu_a = np.ascontiguousarray(np.asarray(cu, np.int32))
+        idx_a = np.ascontiguousarray(np.asarray(idx, np.int32))
+        if idx_a.size == 0:
+            idx_a = np.zeros(1, np.int32)
+        ns = None
+        if nsplit is not None:
+            ns = np.ascontiguousarray(np.asarray(nsplit, np.int32))
+            assert ns.shape == (n,) and np.all(ns >= 1)
+        allow = np.zeros((n, self.rows), np.float64)
+        lallow = np.zeros((n, self.rows), np.float64)
+        lib().fpo_attend_list_eq15(
+            C.byref(self._s), _ptr(kb, C.c_double), _ptr(vb, C.c_double), n, _ptr(segs, C.c_int64),
+            _ptr(cu_a, C.c_int32), _ptr(idx_a, C.c_int32), 1 if correction else 0, 1 if rounding else 0,
+            None if ns is None else _ptr(ns, C.c_int32), float(logit_err), _ptr(out, C.c_double),
+            _ptr(lse, C.c_double), _ptr(allow, C.c_double), _ptr(lallow, C.c_double))
+        if logit_err > 0:
+            return out, lse, allow, lallow
+        return out, lse
+
+    def attend_tile_eq15(self, b, h, I, idx, correction=True, rounding=True, nsplit=1, logit_err=0.0):
+        kb, vb = self.pool()
+        idx = np.ascontiguousarray(np.asarray(idx, np.int32))
+        out = np.zeros((self.rows, self.d), np.float64)
+        lse = np.zeros(self.rows, np.float64)
+        buf = idx if idx.size else np.zeros(1, np.int32)
+        allow = np.zeros(self.rows, np.float64)
+        lallow = np.zeros(self.rows, np.float64)
+        lib().fpo_attend_tile_eq15(C.byref(self._s), _ptr(kb, C.c_double), _ptr(vb, C.c_double), b, h, I,
+                                   _ptr(buf, C.c_int32), idx.size, 1 if correction else 0,
+                                   1 if rounding else 0, int(nsplit), float(logit_err), _ptr(out, C.c_double),
+                                   _ptr(lse, C.c_double), _ptr(allow, C.c_double), _ptr(lallow, C.c_double))
+        if logit_err > 0:
+            return out, lse, allow, lallow
         return out, lse
 
     def attend_tile(self, b, h, I, idx, correction=True, p8=False):

@@ -79,23 +79,44 @@ double fpo_e4m3_decode(uint8_t x) {
   return sign ? -mag : mag;
 }
 
-/* Round-to-nearest-even into E4M3 by exhaustive search over the finite codes,
- * saturating at +-448.  Only used by the optional P-quantisation diagnostic. */
+/* Round-to-nearest-even into E4M3, saturating at +-448.  The non-negative
+ * finite codes 0x00..0x7e decode to strictly increasing values, so the code
+ * below |x| is found by bisection over the codes; of it and the next code the
+ * nearer wins, a tie going to the even mantissa (the code's low bit). */
 double fpo_e4m3_round(double x) {
-  double ax = fabs(x), best = 0.0, bestd = INFINITY;
-  int bestm = 0;
+  double ax = fabs(x);
   if (ax >= 448.0) return x < 0 ? -448.0 : 448.0;
-  for (int c = 0; c < 127; ++c) { /* 0x00..0x7e: every finite non-negative code */
-    double v = fpo_e4m3_decode((uint8_t)c);
-    double dd = fabs(v - ax);
-    int mant = c & 7;
-    if (dd < bestd || (dd == bestd && (mant & 1) == 0 && (bestm & 1) == 1)) {
-      bestd = dd;
-      best = v;
-      bestm = mant;
-    }
+  int lo = 0, hi = 126; /* decode(lo) <= ax < decode(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (fpo_e4m3_decode((uint8_t)mid) <= ax)
+      lo = mid;
+    else
+      hi = mid;
   }
+  double a = fpo_e4m3_decode((uint8_t)lo), b = fpo_e4m3_decode((uint8_t)hi);
+  double best;
+  if (ax - a < b - ax)
+    best = a;
+  else if (ax - a > b - ax)
+    best = b;
+  else
+    best = (lo & 1) == 0 ? a : b;
   return x < 0 ? -best : best;
+}
+
+/* The two E4M3 values around |x| < 448 (lo <= |x| < hi), by the same bisection. */
+static void e4m3_bracket(double ax, double* lo_v, double* hi_v) {
+  int lo = 0, hi = 126;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (fpo_e4m3_decode((uint8_t)mid) <= ax)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  *lo_v = fpo_e4m3_decode((uint8_t)lo);
+  *hi_v = fpo_e4m3_decode((uint8_t)hi);
 }
 
 static double bf16_decode(uint16_t b) {
@@ -131,6 +152,12 @@ static void load_v(const fpo_problem* p, int64_t row, int head, double* out) {
 static double dot(const double* a, const double* b, int n) {
   double s = 0.0;
   for (int i = 0; i < n; ++i) s += a[i] * b[i];
+  return s;
+}
+
+static double absdot(const double* a, const double* b, int n) {
+  double s = 0.0;
+  for (int i = 0; i < n; ++i) s += fabs(a[i] * b[i]);
   return s;
 }
 
@@ -466,8 +493,10 @@ int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, i
  *   logits a_i = sigma q.k_i (i in T), c_J = sigma q.k_bar_J + ln|B_J| (J in C)
  *   O = (sum_T e^{a_i-m} v_i + sum_C e^{c_J-m} v_bar_J) / (sum_T e^{a_i-m} + sum_C e^{c_J-m})
  *   LSE = m + ln(denominator), m = max of all logits.
- * p8 != 0 is a diagnostic of [V2] Eq. 15: every weight e^{a-m} is multiplied by
- * 2^8 and rounded to E4M3 before both sums, and LSE subtracts ln 2^8.
+ * p8 != 0 is an order-free diagnostic of [V2] Eq. 15: every weight e^{a-m},
+ * m the FINAL row maximum, is multiplied by 2^8 and rounded to E4M3 before
+ * both sums, and LSE subtracts ln 2^8.  Eq. 15 itself rounds against the
+ * running maximum: fpo_attend_tile_eq15 below.
  * out is [R][d], lse is [R]; rows past the end of the request are zeroed. */
 void fpo_attend_tile(const fpo_problem* p, const double* kbar, const double* vbar, int b,
                      int h, int64_t I, const int32_t* idx, int64_t T, int correction, int p8,
@@ -545,6 +574,204 @@ void fpo_attend_tile(const fpo_problem* p, const double* kbar, const double* vba
   free(num);
 }
 
+/* [V2] §3.3 Eq. 15 as printed: the online softmax visited step by step, each
+ * E4M3 weight rounded against the RUNNING row maximum m.
+ *
+ * Steps, in the order the pages give them: the listed tiles backwards
+ * (n_t = idx[T - 1 - t], Eq. 17), then the correction chunks appended after
+ * them (Algorithm 1, step 9); a chunk is 64 consecutive blocks (READING: the
+ * chunk width is not printed) and holds the corrected blocks of its range.
+ * W = T + ceil(beta/64) steps in all when correction is on, T otherwise.
+ * Under KV splitting, split u of U takes steps [u ceil(W/U), (u+1) ceil(W/U))
+ * of that sequence (Eq. 18's count partition; READING: the correction chunks
+ * count as steps like the listed tiles) and starts with its own maximum; the
+ * splits are merged exactly by their log-sum-exp.
+ *
+ * Per row and split, for each step with member logits x (keys i <= t of the
+ * tile: a_i = sigma q.k_i; corrected blocks of the chunk: c_J = sigma q.k_bar_J
+ * + ln|B_J|, values v_i / v_bar_J):
+ *   m_new = max(m, max x);  acc *= e^{m - m_new};  den *= e^{m - m_new}
+ *   P_x   = round_e4m3(2^8 e^{x - m_new})   (round = 0: 2^8 e^{x - m_new})
+ *   acc  += sum P_x v_x;  den += sum P_x;  m = m_new
+ * so a weight is rounded once, at the maximum of its own step; later rescales
+ * act on the sums, not on rounded weights.  O = acc / den and LSE = m +
+ * ln(den) - ln 2^8, with the splits merged first.  round = 0 is the same
+ * recurrence with no rounding, which must reproduce fpo_attend_tile's exact
+ * rows (the recurrence, the rescales and the split merge are exact in exact
+ * arithmetic).  nsplit >= 1.  out is [R][d], lse is [R].
+ *
+ * Rounding ties (allow, lallow: optional [R]).  An implementation forms each
+ * logit with some error; take it to be at most logit_err times the logit's
+ * sum of absolute products, A = sigma sum_i |q_i k_i| (the same for a mean,
+ * without its ln|B_J|).  A weight 2^8 e^{x - m} is then known only up to a
+ * factor e^{+-delta}, delta = logit_err (A_x + A_m) with A_m that of the
+ * logit that set the running maximum m; when that interval holds the midpoint
+ * between the weight's two E4M3 neighbours, both roundings are valid.  For
+ * each row, allow bounds how far the output can move (max-abs over the row)
+ * and lallow how far the LSE can move if every such weight took its other
+ * rounding:
+ *   S  = sum over tied weights of f s_i,  SV = sum of f s_i |v_i|_inf
+ *   allow = (SV + S |O|_inf) / (D - S),  lallow = -ln(1 - S / D)
+ * with s_i the gap between the neighbours, f the weight's rescale factor into
+ * the merged sums and D the merged denominator (a first-order bound that holds
+ * while S < D; +inf otherwise).  Both are 0 when round = 0 or logit_err = 0. */
+void fpo_attend_tile_eq15(const fpo_problem* p, const double* kbar, const double* vbar, int b,
+                          int h, int64_t I, const int32_t* idx, int64_t T, int correction,
+                          int round, int nsplit, double logit_err, double* out, double* lse,
+                          double* allow, double* lallow) {
+  int g = group(p), d = p->d;
+  int64_t t0, t1, beta;
+  int nrows = fpo_tile_info(p, b, I, &t0, &t1, &beta);
+  int64_t L = req_len(p, b);
+  int64_t nblk = fpo_blocks_in_req(p, b);
+  int64_t blk0 = fpo_block_offset(p, b);
+  const int64_t CH = 64;
+  int64_t nch = correction ? (beta + CH - 1) / CH : 0;
+  int64_t W = T + nch;
+  if (nsplit < 1) nsplit = 1;
+  int64_t per = (W + nsplit - 1) / nsplit;
+  uint8_t* in_s = (uint8_t*)calloc((size_t)(nblk > 0 ? nblk : 1), 1);
+  for (int64_t e = 0; e < T; ++e) {
+    int64_t J = (int64_t)idx[e] * p->phys / p->block;
+    if (J >= 0 && J < nblk) in_s[J] = 1;
+  }
+  double* qv = (double*)malloc(sizeof(double) * d);
+  double* kv = (double*)malloc(sizeof(double) * d);
+  double* vv = (double*)malloc(sizeof(double) * d);
+  double* acc = (double*)malloc(sizeof(double) * d);
+  double* tot = (double*)malloc(sizeof(double) * d);
+  /* logits and values of one step's members */
+  int64_t cap = p->phys > CH ? p->phys : CH;
+  double* x = (double*)malloc(sizeof(double) * cap);
+  double* xa = (double*)malloc(sizeof(double) * cap); /* sigma sum |q_i k_i| of each logit */
+  double* xv = (double*)malloc(sizeof(double) * cap * d);
+  double* m_u = (double*)malloc(sizeof(double) * nsplit);
+  double* den_u = (double*)malloc(sizeof(double) * nsplit);
+  double* ts_u = (double*)malloc(sizeof(double) * nsplit);  /* tied gaps, in split u's scale */
+  double* tsv_u = (double*)malloc(sizeof(double) * nsplit); /* tied gaps times |v|_inf */
+  double* acc_u = (double*)malloc(sizeof(double) * nsplit * d);
+  for (int r = 0; r < p->rows; ++r) {
+    double* o = out + (size_t)r * d;
+    if (r >= nrows) {
+      for (int i = 0; i < d; ++i) o[i] = 0.0;
+      if (lse) lse[r] = 0.0;
+      if (allow) allow[r] = 0.0;
+      if (lallow) lallow[r] = 0.0;
+      continue;
+    }
+    int64_t pr = I * p->rows + r;
+    int64_t t = q_off(p, b) + pr / g; /* position of the row's query */
+    load_q(p, p->cu[b] + pr / g, h * g + (int)(pr % g), qv);
+    for (int u = 0; u < nsplit; ++u) {
+      double m = -INFINITY, am = 0.0, den = 0.0, ts = 0.0, tsv = 0.0; /* am: A of the maximum */
+      for (int i = 0; i < d; ++i) acc[i] = 0.0;
+      int64_t s0 = (int64_t)u * per, s1 = s0 + per;
+      if (s0 > W) s0 = W;
+      if (s1 > W) s1 = W;
+      for (int64_t st = s0; st < s1; ++st) {
+        /* the step's members */
+        int64_t n = 0;
+        if (st < T) {
+          int64_t tile = idx[T - 1 - st];
+          for (int64_t i = tile * p->phys; i < (tile + 1) * p->phys; ++i) {
+            if (i > t || i >= L) continue;
+            load_k(p, kv_start(p, b) + i, h, kv);
+            load_v(p, kv_start(p, b) + i, h, xv + (size_t)n * d);
+            xa[n] = p->scale * absdot(qv, kv, d);
+            x[n++] = p->scale * dot(qv, kv, d);
+          }
+        } else {
+          int64_t ch = st - T;
+          for (int64_t J = ch * CH; J < (ch + 1) * CH && J < beta; ++J) {
+            if (in_s[J]) continue;
+            const double* vb = kbar_row(p, vbar, blk0, h, J);
+            for (int i = 0; i < d; ++i) xv[(size_t)n * d + i] = vb[i];
+            xa[n] = p->scale * absdot(qv, kbar_row(p, kbar, blk0, h, J), d);
+            x[n++] = p->scale * dot(qv, kbar_row(p, kbar, blk0, h, J), d) + log((double)p->block);
+          }
+        }
+        if (n == 0) continue;
+        double mx = -INFINITY, amx = 0.0;
+        for (int64_t j = 0; j < n; ++j)
+          if (x[j] > mx) {
+            mx = x[j];
+            amx = xa[j];
+          }
+        if (mx > m) {
+          am = amx;
+          double f = m == -INFINITY ? 0.0 : exp(m - mx);
+          den *= f;
+          ts *= f;
+          tsv *= f;
+          for (int i = 0; i < d; ++i) acc[i] *= f;
+          m = mx;
+        }
+        for (int64_t j = 0; j < n; ++j) {
+          double w = 256.0 * exp(x[j] - m);
+          if (round) {
+            if (logit_err > 0.0 && w < 448.0) {
+              double lo, hi;
+              e4m3_bracket(w, &lo, &hi);
+              double mid = 0.5 * (lo + hi), delta = logit_err * (xa[j] + am);
+              if (fabs(log(w / mid)) <= delta) {
+                double vmax = 0.0;
+                for (int i = 0; i < d; ++i)
+                  if (fabs(xv[(size_t)j * d + i]) > vmax) vmax = fabs(xv[(size_t)j * d + i]);
+                ts += hi - lo;
+                tsv += (hi - lo) * vmax;
+              }
+            }
+            w = fpo_e4m3_round(w);
+          }
+          den += w;
+          for (int i = 0; i < d; ++i) acc[i] += w * xv[(size_t)j * d + i];
+        }
+      }
+      m_u[u] = m;
+      den_u[u] = den;
+      ts_u[u] = ts;
+      tsv_u[u] = tsv;
+      for (int i = 0; i < d; ++i) acc_u[(size_t)u * d + i] = acc[i];
+    }
+    /* merge the splits by their maxima */
+    double M = -INFINITY;
+    for (int u = 0; u < nsplit; ++u)
+      if (m_u[u] > M) M = m_u[u];
+    double D = 0.0, S = 0.0, SV = 0.0;
+    for (int i = 0; i < d; ++i) tot[i] = 0.0;
+    for (int u = 0; u < nsplit; ++u) {
+      if (m_u[u] == -INFINITY) continue;
+      double f = exp(m_u[u] - M);
+      D += f * den_u[u];
+      S += f * ts_u[u];
+      SV += f * tsv_u[u];
+      for (int i = 0; i < d; ++i) tot[i] += f * acc_u[(size_t)u * d + i];
+    }
+    double omax = 0.0;
+    for (int i = 0; i < d; ++i) {
+      o[i] = tot[i] / D;
+      if (fabs(o[i]) > omax) omax = fabs(o[i]);
+    }
+    if (lse) lse[r] = M + log(D) - log(256.0);
+    if (allow) allow[r] = S == 0.0 ? 0.0 : S < D ? (SV + S * omax) / (D - S) : INFINITY;
+    if (lallow) lallow[r] = S == 0.0 ? 0.0 : S < D ? -log(1.0 - S / D) : INFINITY;
+  }
+  free(in_s);
+  free(qv);
+  free(kv);
+  free(vv);
+  free(acc);
+  free(tot);
+  free(x);
+  free(xa);
+  free(xv);
+  free(m_u);
+  free(den_u);
+  free(ts_u);
+  free(tsv_u);
+  free(acc_u);
+}
+
 /* Dense causal softmax attention of the same rows ([V2] §3.2 Eq. 4 left). */
 void fpo_dense_tile(const fpo_problem* p, int b, int h, int64_t I, double* out, double* lse) {
   int g = group(p), d = p->d;
@@ -606,6 +833,27 @@ void fpo_attend_list(const fpo_problem* p, const double* kbar, const double* vba
     else
       fpo_attend_tile(p, kbar, vbar, b, h, I, idx + cu[segs[n]], cu[segs[n] + 1] - cu[segs[n]],
                       correction, p8, o, l);
+  }
+}
+
+/* [V2] Eq. 15 rows of a list of segments (OpenMP over segments): cu, idx
+ * indexed by segment id as above; nsplit[n] (NULL: 1) is the split count of
+ * the n-th listed segment; allow / lallow ([nlist][R], optional) as in
+ * fpo_attend_tile_eq15. */
+void fpo_attend_list_eq15(const fpo_problem* p, const double* kbar, const double* vbar,
+                          int64_t nlist, const int64_t* segs, const int32_t* cu, const int32_t* idx,
+                          int correction, int round, const int32_t* nsplit, double logit_err,
+                          double* out, double* lse, double* allow, double* lallow) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nlist; ++n) {
+    int32_t b, h;
+    int64_t I;
+    fpo_segment_coords(p, segs[n], &b, &h, &I);
+    fpo_attend_tile_eq15(p, kbar, vbar, b, h, I, idx + cu[segs[n]], cu[segs[n] + 1] - cu[segs[n]],
+                         correction, round, nsplit ? nsplit[n] : 1, logit_err,
+                         out + (size_t)n * p->rows * p->d, lse ? lse + (size_t)n * p->rows : NULL,
+                         allow ? allow + (size_t)n * p->rows : NULL,
+                         lallow ? lallow + (size_t)n * p->rows : NULL);
   }
 }
 

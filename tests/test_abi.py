@@ -38,6 +38,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_binding_lists_exactly_the_declared_functions():
+    """The binding's export list names every function the header declares, and nothing else."""
+    assert sorted(_fp().EXPORTS) == declared_functions()
+
+
+def test_library_exports_match_the_header():
+    """The shared object's exported fp_* functions are exactly the header's."""
+    lib = os.path.join(ROOT, "block_sparse_long_mean_amd", "libfp.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines()
+                       if ln.split() and ln.split()[-1].startswith("fp_") and " T " in ln})
+    assert exported == declared_functions()
+
+
 def _problem(fp, lengths=(1000, 300), hq=32, hkv=4, dtype=1, **kw):
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     p = fp.Problem()
@@ -250,3 +264,26 @@ def test_empty_batch_launches_nothing():
     assert lib.fp_sparse_attn(C.byref(p), C.byref(sp), dummy, dummy, dummy, dummy, dummy, dummy, 1, dummy, None,
                               dummy, ws, None) == 0
     assert lib.fp_dense_attn(C.byref(p), dummy, dummy, dummy, dummy, None, dummy, ws, None) == 0
+
+
+def test_step_count_bound_near_int32_limit():
+    """The scheduler sums per-segment step counts (listed tiles plus correction
+    chunks) in int32.  Two E4M3 requests of 1,048,576 and L2 tokens with 31
+    heads, g = 1: for some L2 the worst-case index still fits int32 but the
+    worst-case step count does not; such a problem is refused before anything
+    is sized, while a slightly shorter L2 is accepted."""
+    fp = _fp()
+    refused = accepted = None
+    for L2 in range(147456, 188416, 4096):
+        p, cu = _problem(fp, lengths=(8192 * 128, L2), hq=31, hkv=31, dtype=2, descale=0x1000)
+        st, out = _sizes(fp, p)
+        msg = fp.lib_handle().fp_last_error().decode()
+        if st == 0:
+            accepted = (L2, out.idx_capacity)
+        elif "attention steps" in msg:
+            assert st == -2
+            refused = L2
+            break
+    assert accepted is not None and refused is not None, (accepted, refused)
+    assert accepted[1] <= 2**31 - 1 and accepted[0] < refused
+

@@ -16,12 +16,9 @@ import pytest
 import torch
 
 from block_sparse_long_mean_amd import configs
-from tests.gpu_harness import GpuRun, check_e4m3, compare_attn, compare_csr, oracle_for, sample_segments
+from tests.gpu_harness import GpuRun, check_rows, compare_attn, compare_csr, oracle_for, sample_segments
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"bf16": (2e-2, 2e-3), "e4m3": (6e-2, 1e-2)}
-
 
 def _note(msg):
     print(msg, flush=True)
@@ -47,15 +44,9 @@ def _check_pool(run, P):
 
 
 def _attn_check(run, P, segs, cu, idx, dtype, correction=True):
+    assert run.batch.dtype == dtype
     out, lse = run.attn(correction=correction)
-    tmax, tmean = TOL[dtype]
-    if dtype == "e4m3":
-        mx, mean = check_e4m3(P, out, lse, segs, cu, idx, correction, tmax, tmean, note=_note)
-    else:
-        mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=correction)
-        _note(f"  attention corr={correction}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
-        assert mx <= tmax and mean <= tmean
-    return mx, mean
+    return check_rows(run, P, out, lse, segs, cu, idx, correction=correction, note=_note)
 
 
 def test_32k_full_csr_sampled_attention():

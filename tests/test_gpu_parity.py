@@ -10,13 +10,11 @@ import pytest
 import torch
 
 from block_sparse_long_mean_amd import configs, synth
-from tests.gpu_harness import GpuRun, check_e4m3, compare_attn, compare_csr, oracle_for, sample_segments
+from tests.gpu_harness import (E4M3_EXACT_MAX_EQ15_OVER, GpuRun, check_rows, compare_attn, compare_csr, oracle_for,
+                               sample_segments)
 from tests.helpers import oracle_problem
 
 pytestmark = pytest.mark.gpu
-
-TOL = {"bf16": (2e-2, 2e-3), "f32": (2e-2, 2e-3), "e4m3": (6e-2, 1e-2)}
-
 
 def _small(dtype, lengths=(1000, 2500, 333), seed=7):
     b = synth.make_batch(list(lengths), 32, 4, 128, seed=seed, dtype="f32" if dtype == "f32" else "bf16",
@@ -98,15 +96,9 @@ def test_sparse_attention_matches_oracle(dtype, correction):
     P = oracle_for(run)
     segs = sample_segments(P, 96, seed=1)
     out, lse = run.attn(correction=correction)
-    tmax, tmean = TOL[dtype]
-    if dtype == "e4m3":
-        # Eq. 15 rounds every probability to E4M3; the oracle's own evaluation of that
-        # rounding sets the scale of the error against the exact softmax.
-        check_e4m3(P, out, lse, segs, cu, idx, correction, tmax, tmean)
-    else:
-        mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=correction)
-        print(f"{dtype} corr={correction}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
-        assert mx <= tmax and mean <= tmean
+    # on this batch Eq. 15's own rows lie 6.64e-2 from the exact ones (E4M3)
+    check_rows(run, P, out, lse, segs, cu, idx, correction=correction,
+               exact_max=E4M3_EXACT_MAX_EQ15_OVER if dtype == "e4m3" else None)
     assert run.device_error() == 0
 
 
@@ -118,10 +110,7 @@ def test_dense_attention_matches_oracle(dtype):
     P = oracle_for(run)
     segs = sample_segments(P, 64, seed=2)
     out, lse = run.attn(dense=True)
-    mx, mean, _ = compare_attn(P, out, lse, segs, dense=True)
-    print(f"dense {dtype}: max {mx:.3e} mean {mean:.3e}")
-    tmax, tmean = TOL[dtype]
-    assert mx <= tmax and mean <= tmean
+    check_rows(run, P, out, lse, segs, dense=True)
 
 
 def test_alpha_zero_sparse_equals_dense_on_gpu():
@@ -210,19 +199,11 @@ def test_group_sizes(hq, hkv, dtype):
     n, amb = compare_csr(P, cu, idx, 0.1, 2, 4)
     print(f"  CSR: {n} segments, {amb} band differences")
     segs = sample_segments(P, 64, seed=11)
-    tmax, tmean = TOL[dtype]
     for corr in (True, False):
         out, lse = run.attn(correction=corr)
-        if dtype == "e4m3":
-            check_e4m3(P, out, lse, segs, cu, idx, corr, tmax, tmean)
-        else:
-            mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
-            print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
-            assert mx <= tmax and mean <= tmean
+        check_rows(run, P, out, lse, segs, cu, idx, correction=corr)
     out, lse = run.attn(dense=True)
-    mx, mean, _ = compare_attn(P, out, lse, segs, dense=True)
-    print(f"  dense: max {mx:.3e} mean {mean:.3e}")
-    assert mx <= tmax and mean <= tmean
+    check_rows(run, P, out, lse, segs, dense=True)
     assert run.device_error() == 0
 
 
@@ -238,15 +219,11 @@ def test_edge_lengths(dtype):
     P = oracle_for(run)
     compare_csr(P, cu, idx, 0.1, 1, 1)
     segs = list(range(P.num_segments()))
-    tmax, tmean = TOL[dtype]
     for corr in (True, False):
         out, lse = run.attn(correction=corr)
-        mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
-        print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
-        assert mx <= tmax and mean <= tmean
+        check_rows(run, P, out, lse, segs, cu, idx, correction=corr)
     out, lse = run.attn(dense=True)
-    mx, mean, _ = compare_attn(P, out, lse, segs, dense=True)
-    assert mx <= tmax and mean <= tmean
+    check_rows(run, P, out, lse, segs, dense=True)
     assert run.device_error() == 0
 
 
@@ -266,9 +243,7 @@ def test_longest_request():
     n, amb = compare_csr(P, cu, idx, 0.1, 2, 4, segs=segs)
     print(f"  CSR: {n} sampled segments, {amb} band differences; entries {len(idx)}")
     out, lse = run.attn(correction=True)
-    mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=True)
-    print(f"  attention: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}")
-    assert mx <= 2e-2 and mean <= 2e-3
+    check_rows(run, P, out, lse, segs, cu, idx, correction=True)
     assert run.device_error() == 0
 
 
@@ -287,15 +262,9 @@ def test_long_tile_lists(dtype):
     assert sizes.max() > 64, int(sizes.max())
     segs = sorted(set(np.argsort(sizes)[-12:].tolist()) | {0})
     compare_csr(P, cu, idx, 0.0, 2, 4, segs=segs)
-    tmax, tmean = TOL[dtype]
     for corr in (True, False):
         out, lse = run.attn(correction=corr)
-        if dtype == "e4m3":
-            check_e4m3(P, out, lse, segs, cu, idx, corr, tmax, tmean)
-        else:
-            mx, mean, lmx = compare_attn(P, out, lse, segs, cu, idx, correction=corr)
-            print(f"  corr={corr}: max {mx:.3e} mean {mean:.3e} lse {lmx:.3e}", flush=True)
-            assert mx <= tmax and mean <= tmean
+        check_rows(run, P, out, lse, segs, cu, idx, correction=corr)
     if dtype == "bf16":
         s_out, _ = run.attn(correction=True)
         d_out, _ = run.attn(dense=True)

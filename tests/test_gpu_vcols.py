@@ -12,12 +12,9 @@ import pytest
 import torch
 
 from block_sparse_long_mean_amd import configs, synth
-from tests.gpu_harness import GpuRun, check_e4m3, compare_attn, oracle_for, sample_segments
+from tests.gpu_harness import GpuRun, check_rows, oracle_for, sample_segments
 
 pytestmark = pytest.mark.gpu
-
-TMAX, TMEAN = 6e-2, 1e-2
-
 
 def _note(msg):
     print(msg, flush=True)
@@ -54,14 +51,12 @@ def test_vcols_contiguous_matches_oracle_and_rows():
     for corr in (True, False):
         oc, lc = rc.attn(correction=corr)
         orow, lrow = rr.attn(correction=corr)
-        check_e4m3(P, oc, lc, segs, cu, idx, corr, TMAX, TMEAN, note=_note)
+        check_rows(rc, P, oc, lc, segs, cu, idx, correction=corr, note=_note)
         d = float((oc.float() - orow.float()).abs().max())
         _note(f"  corr={corr}: columns vs rows max {d:.2e}")
         assert torch.isfinite(oc.float()).all() and d <= 2e-2
     od, ld = rc.attn(dense=True)
-    mx, mean, _ = compare_attn(P, od, ld, segs, dense=True)
-    _note(f"  dense: max {mx:.3e} mean {mean:.3e}")
-    assert mx <= TMAX and mean <= TMEAN
+    check_rows(rc, P, od, ld, segs, dense=True, note=_note)
     assert rc.device_error() == 0 and rr.device_error() == 0
 
 
@@ -94,5 +89,5 @@ def test_vcols_128k_sampled():
     P = oracle_for(run)
     segs = sample_segments(P, 48, seed=7)
     out, lse = run.attn(correction=True)
-    check_e4m3(P, out, lse, segs, cu, idx, True, TMAX, TMEAN, note=_note)
+    check_rows(run, P, out, lse, segs, cu, idx, correction=True, note=_note)
     assert run.device_error() == 0
