@@ -410,6 +410,33 @@ static fp_status run_attn(const fp_problem* prob, const void* q, const void* k, 
   return launch_attention(prob, pr, q, k, v, cu, idx, means, dense, correction, out, lse, ws, stream);
 }
 
+// ---- scratch of the no-allocation entry point ----------------------------
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns for the current device, taken once
+// per device and kept in the table below.
+constexpr size_t kStaticScratchBytes = FP_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+static std::mutex g_scratch_mu;
+static std::vector<void*> g_scratch_ptr;  // per device: scratch's address there, or null until first use
+
+static fp_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(FP_ERR_LAUNCH, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FP_ERR_LAUNCH, "hipGetSymbolAddress of the static scratch failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP_OK;
+}
 
 fp_status fp_sparse_attn(const fp_problem* prob, const fp_select_params* params, const void* q, const void* k,
                          const void* v, const int32_t* cu, const int32_t* idx, const void* means,
@@ -418,6 +445,28 @@ fp_status fp_sparse_attn(const fp_problem* prob, const fp_select_params* params,
   fp_status s = validate_params(params);
   if (s != FP_OK) return s;
   return run_attn(prob, q, k, v, cu, idx, means, 0, mean_correction ? 1 : 0, out, lse, ws, ws_bytes, stream);
+}
+
+fp_status fp_sparse_attn_static(const fp_problem* prob, const fp_select_params* params, const void* q,
+                                const void* k, const void* v, const int32_t* cu, const int32_t* idx,
+                                const void* means, int32_t mean_correction, void* out, float* lse, void* stream) {
+  fp_status s = validate_params(params);
+  if (s != FP_OK) return s;
+  Prepared pr;
+  if ((s = validate_problem(prob, &pr.hg)) != FP_OK) return s;
+  if (!q || !k || !v || !out || !cu || !idx || !means)
+    return fail(FP_ERR_INVALID_ARG, "q, k, v, out, cu, idx and means are required");
+  pr.ml = means_layout(prob, pr.hg);
+  pr.sp.umax = 1;  // no KV splitting: no split partials in the scratch
+  pr.sp.min_split = 4;
+  pr.wl = ws_layout(prob, pr.hg, pr.sp, /*with_select=*/false);
+  if (pr.wl.total > kStaticScratchBytes)
+    return fail(FP_ERR_WORKSPACE_TOO_SMALL, "this problem needs %zu bytes of scratch; the static scratch holds %zu",
+                pr.wl.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != FP_OK) return s;
+  pr.g = make_geo(prob, pr.hg, (char*)ws, pr.wl);
+  return launch_attention(prob, pr, q, k, v, cu, idx, means, 0, mean_correction ? 1 : 0, out, lse, ws, stream);
 }
 
 fp_status fp_dense_attn(const fp_problem* prob, const void* q, const void* k, const void* v, void* out,

@@ -63,6 +63,8 @@ _lib.fp_select.argtypes = [_P, _SP, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp, _vp
 _lib.fp_sparse_attn.restype = C.c_int
 _lib.fp_sparse_attn.argtypes = [_P, _SP, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, _vp, _vp, _vp,
                                 C.c_size_t, _vp]
+_lib.fp_sparse_attn_static.restype = C.c_int
+_lib.fp_sparse_attn_static.argtypes = [_P, _SP, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int32, _vp, _vp, _vp]
 _lib.fp_dense_attn.restype = C.c_int
 _lib.fp_dense_attn.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
 _lib.fp_block_mass.restype = C.c_int
@@ -76,7 +78,8 @@ _lib.fp_status_string.argtypes = [C.c_int]
 _lib.fp_last_error.restype = C.c_char_p
 _lib.fp_last_error.argtypes = []
 
-EXPORTS = ["fp_query_sizes", "fp_pool", "fp_select", "fp_sparse_attn", "fp_dense_attn", "fp_block_mass",
+EXPORTS = ["fp_query_sizes", "fp_pool", "fp_select", "fp_sparse_attn", "fp_sparse_attn_static", "fp_dense_attn",
+           "fp_block_mass",
            "fp_read_device_error", "fp_block_base", "fp_status_string", "fp_last_error"]
 
 
@@ -189,6 +192,13 @@ def sparse_attn(batch: Batch, params: SelectParams, q, k, v, bufs: Buffers, out,
     _check(_lib.fp_sparse_attn(batch.ptr, C.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(bufs.cu),
                                _ptr(bufs.idx), _ptr(bufs.means), 1 if correction else 0, _ptr(out),
                                _ptr(lse), _ptr(bufs.ws), bufs.ws.numel(), _stream()))
+
+
+def sparse_attn_static(batch: Batch, params: SelectParams, q, k, v, cu, idx, means, out, lse=None,
+                       correction=True):
+    """fp_sparse_attn on the library's static scratch (no workspace argument)."""
+    _check(_lib.fp_sparse_attn_static(batch.ptr, C.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(cu), _ptr(idx),
+                                      _ptr(means), 1 if correction else 0, _ptr(out), _ptr(lse), _stream()))
 
 
 def dense_attn(batch: Batch, q, k, v, bufs: Buffers, out, lse=None):

@@ -23,7 +23,9 @@
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
- *     every buffer; the library allocates no device memory.
+ *     every buffer; the library allocates no device memory.  Its only device
+ *     state is the static scratch of fp_sparse_attn_static (a file-scope
+ *     array each GPU holds from library load to process end).
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
  *     is the default stream).  Only fp_read_device_error synchronises.
  *   - Host-visible arguments are validated before anything is launched; a bad
@@ -182,6 +184,28 @@ fp_status fp_sparse_attn(const fp_problem* prob, const fp_select_params* params,
                          const void* k, const void* v, const int32_t* cu, const int32_t* idx,
                          const void* means, int32_t mean_correction, void* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation as fp_sparse_attn (every argument means what it means there),
+ * with the library's own static device scratch in place of a caller
+ * workspace.  Each GPU the library runs on holds FP_STATIC_SCRATCH_BYTES of
+ * it until the process ends; the scratch's address on the current device is
+ * looked up on the first call there.  KV splitting is off (a work unit is a
+ * whole query tile), so outputs equal fp_sparse_attn's run with
+ * FP_MAX_SPLITS=1 bit for bit.  A problem whose workspace exceeds the scratch
+ * (about 80 bytes per CSR segment plus a few KB) returns
+ * FP_ERR_WORKSPACE_TOO_SMALL with nothing launched; no device memory is
+ * allocated on any path.  Every call on a GPU uses that GPU's one scratch:
+ * calls that overlap on one GPU (two streams, two host threads) race and
+ * must be ordered by the caller.  The device error flag of these calls lives
+ * in the scratch and is not readable through fp_read_device_error; malformed
+ * device data still turns the affected rows into NaN. */
+#define FP_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+fp_status fp_sparse_attn_static(const fp_problem* prob, const fp_select_params* params, const void* q,
+                                const void* k, const void* v, const int32_t* cu, const int32_t* idx,
+                                const void* means, int32_t mean_correction, void* out, float* lse,
+                                void* stream);
 
 /* Dense causal attention of the same problem through the same kernel
  * ([V2] §4.1: the dense reference that shares the sparse operator's

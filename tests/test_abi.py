@@ -287,3 +287,23 @@ def test_step_count_bound_near_int32_limit():
     assert accepted is not None and refused is not None, (accepted, refused)
     assert accepted[1] <= 2**31 - 1 and accepted[0] < refused
 
+
+def test_static_scratch_entry_point_checks_on_the_host():
+    """fp_sparse_attn_static: missing buffers and problems whose workspace exceeds
+    the static scratch are refused before anything touches a device."""
+    fp = _fp()
+    lib = fp.lib_handle()
+    params = fp.select_params(0.1, 2, 4)
+    p, cu = _problem(fp)
+    st = lib.fp_sparse_attn_static(C.byref(p), C.byref(params), None, None, None, None, None, None, 1, None,
+                                   None, None)
+    assert st == -1
+    # 4096 requests of 16K tokens, MHA with one head: 524,288 segments need ~42 MB of scratch
+    lengths = (16384,) * 4096
+    p, cu = _problem(fp, lengths=lengths, hq=1, hkv=1)
+    st, out = _sizes(fp, p)
+    assert st == 0 and out.n_segments == 4096 * 128
+    dummy = 0x1000  # never dereferenced: the size check refuses first
+    st = lib.fp_sparse_attn_static(C.byref(p), C.byref(params), dummy, dummy, dummy, dummy, dummy, dummy, 1,
+                                   dummy, None, None)
+    assert st == -3 and "static scratch" in lib.fp_last_error().decode()
