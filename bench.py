@@ -190,8 +190,10 @@ def measure(case, steps, warmup, correction=True):
 
 
 def cpu_baseline(batch, w, n_seg=64):
-    """The oracle (fp64, OpenMP over segments) on a bounded sample: pooling of every
-    block, then scoring, selection and mean-corrected attention of n_seg segments."""
+    """The oracle (fp64, OpenMP over segments on every host thread) on a bounded
+    sample: pooling of every block, then scoring, selection and mean-corrected
+    attention of n_seg segments.  Also reports the labelled extrapolation of one
+    whole call: pooling time + the sample's wall time scaled to every segment."""
     import oracle
     from tests.helpers import oracle_problem
 
@@ -201,17 +203,12 @@ def cpu_baseline(batch, w, n_seg=64):
     t_pool = time.time() - t0
     nseg = P.num_segments()
     rng = np.random.default_rng(0)
+    n_seg = min(n_seg, nseg // 2)
     segs = sorted(2 * x for x in rng.choice(nseg // 2, size=n_seg, replace=False).tolist())  # non-adjacent
     t1 = time.time()
-    cu = np.zeros(nseg + 1, np.int32)
-    lists = []
-    off = 0
-    for s in segs:
-        e, sel, amb, lst = P.segment_select(s, w.alpha, w.sink_blocks, w.window_blocks)
-        cu[s], cu[s + 1] = off, off + len(lst)
-        off += len(lst)
-        lists.append(lst)
-    P.attend_segments(segs, cu, np.concatenate(lists), correction=True)
+    cu, idx = P.select_segments(segs, w.alpha, w.sink_blocks, w.window_blocks)
+    t_sel = time.time() - t1
+    P.attend_segments(segs, cu, idx, correction=True)
     t_seg = time.time() - t1
     flops = 0.0
     for s in segs:
@@ -223,11 +220,38 @@ def cpu_baseline(batch, w, n_seg=64):
     total_rows = batch.total * batch.hq
     sample_rows = n_seg * 128
     t = t_seg + t_pool * sample_rows / total_rows
+    full_s = t_pool + t_seg * nseg / n_seg
     return {"value": flops / t / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{n_seg} of {nseg} (KV head, query tile) segments: scoring and selection "
-                      f"(serial) and mean-corrected attention (OpenMP), plus pooling of all blocks "
-                      f"charged pro rata (pool {t_pool:.1f} s, segments {t_seg:.1f} s)"}
+            "sample": f"{n_seg} of {nseg} (KV head, query tile) segments: scoring, selection and "
+                      f"mean-corrected attention (all OpenMP over segments), plus pooling of all blocks "
+                      f"charged pro rata (pool {t_pool:.2f} s, selection {t_sel:.1f} s, segments {t_seg:.1f} s)",
+            "extrapolated_full_call_s": full_s,
+            "extrapolated_note": "extrapolation, not a measurement: pooling of every block + the sampled "
+                                 "segments' wall time x (all segments / sampled segments), on the same threads",
+            "nproc": os.cpu_count()}
+
+
+def other_workloads(args):
+    """The 32K layer and the paged varlen batch, timed like the headline workload
+    (select, attention, density, algorithmic attention TFLOP/s and its fraction
+    of the bf16 MFMA peak, dense-equivalent rate of the step)."""
+    out = {}
+    for w in (configs.L32K, configs.VARLEN):
+        batch, paged = w.make()
+        case = Case(batch, paged, w.alpha, w.sink_blocks, w.window_blocks)
+        m = measure(case, max(3, args.steps // 2), max(1, args.warmup))
+        F = dense_flops(batch.lengths, batch.hq, batch.q_lengths)
+        alg = m["attn_alg_flop"] / (m["attn_ms"] / 1e3) / 1e12
+        out[w.name] = {"num_reqs": len(batch.lengths), "total_tokens": int(sum(batch.lengths)),
+                       "paged": bool(w.page_size), "select_ms": m["select_ms"], "attn_ms": m["attn_ms"],
+                       "step_ms": m["step_ms"], "density": m["density"],
+                       "eff_tflops": F / (m["step_ms"] / 1e3) / 1e12, "attn_alg_tflops": alg,
+                       "attn_roofline_frac": alg / PEAK[batch.dtype],
+                       "mfma_util_executed": m["attn_exec_flop"] / (m["attn_ms"] / 1e3) / 1e12 / PEAK[batch.dtype]}
+        del case, batch, paged
+        torch.cuda.empty_cache()
+    return out
 
 
 def sweep(args):
@@ -365,7 +389,7 @@ def main():
     ap.add_argument("--config", default=configs.L128K.name, choices=sorted(configs.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / fp8 / alpha variants")
-    ap.add_argument("--cpu-segments", type=int, default=2048)
+    ap.add_argument("--cpu-segments", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     ap.add_argument("--sweep", action="store_true",
@@ -456,6 +480,7 @@ def main():
             variants["fp8_vcols_dense_ms"] = dd
             del c8
         extra["variants"] = variants
+        extra["other_workloads"] = other_workloads(args)
     res = {
         "metric": METRIC,
         "value": F / (main_m["step_ms"] / 1e3) / 1e12,

@@ -88,6 +88,9 @@ def lib():
         L.fpo_select_all.restype = C.c_int64
         L.fpo_select_all.argtypes = [P, dp, C.c_double, C.c_int, C.c_int, C.c_int, i32p, i32p,
                                      C.c_int64, dp, u8p, C.c_int64]
+        L.fpo_select_list.restype = None
+        L.fpo_select_list.argtypes = [P, dp, C.c_double, C.c_int, C.c_int, C.c_int, C.c_int64, i64p, C.c_int64,
+                                      i32p, i32p]
         L.fpo_attend_tile.restype = None
         L.fpo_attend_tile.argtypes = [P, dp, dp, C.c_int, C.c_int, C.c_int64, i32p, C.c_int64,
                                       C.c_int, C.c_int, dp, dp]
@@ -283,6 +286,27 @@ class Problem:
         if want_energies:
             return cu, idx[:n], e, amb.astype(bool)
         return cu, idx[:n]
+
+    def select_segments(self, segs, alpha, n_sink, n_win, form=2):
+        """Tile lists of the listed segments (OpenMP over them): a CSR (cu, idx)
+        over ALL segments of the problem in which only the listed ones are
+        non-empty."""
+        kb, _ = self.pool()
+        segs = np.ascontiguousarray(np.asarray(segs, np.int64))
+        stride = 2 * self.max_candidates()
+        lists = np.zeros((len(segs), stride), np.int32)
+        counts = np.zeros(len(segs), np.int32)
+        lib().fpo_select_list(C.byref(self._s), _ptr(kb, C.c_double), alpha, n_sink, n_win, form, len(segs),
+                              _ptr(segs, C.c_int64), stride, _ptr(lists, C.c_int32), _ptr(counts, C.c_int32))
+        nseg = self.num_segments()
+        cnt = np.zeros(nseg, np.int64)
+        cnt[segs] = counts
+        cu = np.zeros(nseg + 1, np.int32)
+        cu[1:] = np.cumsum(cnt)
+        idx = np.zeros(max(int(cu[-1]), 1), np.int32)
+        for n, s in enumerate(segs):
+            idx[cu[s]:cu[s + 1]] = lists[n, :counts[n]]
+        return cu, idx[: int(cu[-1])]
 
     # -- attention ------------------------------------------------------
     def attend_segments(self, segs, cu=None, idx=None, dense=False, correction=True, p8=False):

@@ -480,6 +480,30 @@ int64_t fpo_select_all(const fpo_problem* p, const double* kbar, double alpha, i
   return total;
 }
 
+/* Index of a list of segments (OpenMP over the list): scoring, selection and
+ * CSR expansion of segs[n] into lists + n * stride (stride >= 2 * the
+ * segment's candidate count), its length into counts[n]. */
+void fpo_select_list(const fpo_problem* p, const double* kbar, double alpha, int n_sink, int n_win,
+                     int form, int64_t nlist, const int64_t* segs, int64_t stride, int32_t* lists,
+                     int32_t* counts) {
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t n = 0; n < nlist; ++n) {
+    int32_t b, h;
+    int64_t I, t0, t1, beta;
+    fpo_segment_coords(p, segs[n], &b, &h, &I);
+    fpo_tile_info(p, b, I, &t0, &t1, &beta);
+    int64_t nc = t1 / p->block + 1;
+    double* e = (double*)malloc(sizeof(double) * nc);
+    uint8_t* sel = (uint8_t*)malloc(nc);
+    fpo_score_tile(p, kbar, b, h, I, form, e);
+    fpo_select_tile(e, nc, beta, alpha, n_sink, n_win, sel, NULL);
+    counts[n] = (int32_t)fpo_csr_tile(sel, nc, t1, p->phys, p->block, NULL);
+    if (counts[n] <= stride) fpo_csr_tile(sel, nc, t1, p->phys, p->block, lists + n * stride);
+    free(e);
+    free(sel);
+  }
+}
+
 /* ------------------------------------------------------------------ */
 /* attention of one tile with mean correction ([V2] §3.2 Eq. 4-6)       */
 /* ------------------------------------------------------------------ */

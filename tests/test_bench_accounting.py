@@ -76,3 +76,16 @@ def test_segment_geometry_and_recall_stats():
     assert abs(st["am_gm_ratio_corrected"] - corr_s / corr_m) < 1e-12
     assert st["exact_rule_block_recall"] == rec_n / rec_d
     assert 0 <= st["missed_after_correction"] <= st["missed_without_correction"]
+
+
+def test_segment_list_selection_matches_the_whole_index():
+    """The CPU baseline's OpenMP selection over a segment list gives each listed
+    segment exactly the tile list of the whole-problem selection."""
+    b = synth.make_batch([900, 2100, 333], 16, 4, 128, seed=13, dtype="bf16", clusters=True, diag_bias=True)
+    P = oracle_problem(b)
+    cu, idx = P.select_all(0.1, 2, 4)
+    segs = [0, 3, 40, 41, P.num_segments() - 1]
+    cu2, idx2 = P.select_segments(segs, 0.1, 2, 4)
+    for s in range(P.num_segments()):
+        want = idx[cu[s]:cu[s + 1]] if s in segs else idx[:0]
+        np.testing.assert_array_equal(idx2[cu2[s]:cu2[s + 1]], want)
