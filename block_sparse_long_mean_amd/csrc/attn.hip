@@ -120,8 +120,10 @@ struct Cfg {
   // e4m3: the lo part of the pooled keys of a correction step (k rows again)
   static constexpr int LOOFF = KBYTES + VBYTES + PENBYTES;
   static constexpr int STAGE = LOOFF + (DT == kE4M3 ? KBYTES : 0);
-  static constexpr int SELOFF = DT == kBF16 ? PipeL::SEL : 2 * STAGE;  // selection bitmask of the unit
-  static constexpr int LDS = DT == kBF16 ? PipeL::LDS : 2 * STAGE + (kMaxBlocks / 32 + 8) * 4;
+  // e4m3 pipelined loop: three rotating correction-offset tables after the stages
+  static constexpr int PEN3 = 2 * STAGE;
+  static constexpr int SELOFF = DT == kBF16 ? PipeL::SEL : DT == kE4M3 ? PEN3 + 3 * 256 : 2 * STAGE;  // selection bitmask
+  static constexpr int LDS = DT == kBF16 ? PipeL::LDS : SELOFF + (kMaxBlocks / 32 + 8) * 4;
   static constexpr int NM0 = kD / (2 * KPL);     // MFMAs per 32x32 logit tile
   static constexpr int NM1 = kTile / (2 * KPL);  // MFMAs per 32-column output tile
   static constexpr int WGS = DT == kF32 ? 1 : 2; // workgroups per CU
@@ -147,9 +149,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-// 16 bytes per lane from a buffer resource straight into LDS at lds + 16 * lane.
+// 16 bytes per lane from a buffer resource straight into LDS at lds + 16 * lane
+// (lds is wave-uniform; it goes to M0).  Issued as inline assembly: for the
+// load builtin the compiler cannot tell one LDS stage from the other, and it
+// then waits for every DMA in flight before the next LDS read, which is the
+// read of the stage being computed while the other one fills.  The DMA's
+// completion is made explicit instead: every stage is published by wait_vmem()
+// and a barrier before any wave reads it.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, (int)voff, 0, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
 }
 // Transpose reads (see the operand builders below for the lane layout).
 __device__ __forceinline__ i16x4 lds_tr16(const char* p) {
@@ -177,6 +186,10 @@ __device__ __forceinline__ float max_halves(float x) {
   const float2 p = with_other_half(x);
   return fmaxf(p.x, p.y);
 }
+
+// An MFMA accumulator held in place: the MFMA that produced it issues before
+// this point and nothing moves it past (the asm reads and rewrites it).
+__device__ __forceinline__ void hold(f32x16& x) { asm volatile("" : "+v"(x)); }
 
 // An empty use of a register value: it must be computed before this point.
 template <typename V>
@@ -1123,6 +1136,318 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       }
     };
 
+    if constexpr (DT == kE4M3 && !VC) {
+      // ---- e4m3 mainloop, software-pipelined across steps.
+      // Iteration k (step s_k) starts with s_k's logits in S, computed by the
+      // previous iteration, and with P(s_{k-1}), the rounded weights of the step
+      // before.  It issues the row-sum MFMA and PV(s_{k-1}) (4 MFMAs) with the
+      // softmax of s_k in pieces between them, writes P(s_k) once PV(s_{k-1})
+      // has read P, applies the (rare) rescale for a raised maximum, and ends
+      // with QK(s_{k+1}) into S (4 MFMAs, 8 for a correction chunk: hi and the
+      // 2^-4-scaled lo part).  One logit set and one weight set, so the loop
+      // body fits the register budget of two waves per SIMD.  Stage par holds
+      // K(s_{k+1}) and V(s_{k-1}); the iteration's DMA fills the other stage
+      // with K(s_{k+2}) and V(s_k), whose previous contents were last read
+      // before the previous barrier.  One barrier per iteration.  Correction
+      // offsets rotate through three tables (those of s_k, s_{k+1} and s_{k+2}
+      // are live at once).  Eq. 15: the weights of s_k are rounded against the
+      // running maximum after s_k's own logits; the rescale follows PV(s_{k-1}),
+      // so it covers every step before s_k.
+      using OpE = i32x8;
+      constexpr int PEN3 = C::PEN3;
+      // per-lane LDS byte offsets (from smem) of the operand reads; stage, key
+      // tile and key group are immediates on top
+      uint32_t ka[4], va[4];
+      {
+        const int sw = swz_k<DT>(col);  // rows jt*32 + col share it: jt*32 >> 1 has no low 3 bits
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int part = 0; part < 2; ++part)
+            ka[2 * m + part] = (uint32_t)(col * C::ROWB + (((4 * m + 2 * half + part) ^ sw) << 4));
+        const int k16 = lane & 15;
+        const int i = k16 >> 1;
+        const int row = 8 * (i >> 2) + 4 * half + (i & 3);  // + 16 tt (immediate)
+        const int sv = swz_v<DT>(row);                      // the same for row + 16 tt
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int colb = nt * 32 + 16 * ((lane >> 4) & 1) + 8 * (k16 & 1);
+          va[nt] = (uint32_t)(C::KBYTES + row * C::ROWB + (((colb >> 4) ^ sv) << 4) + (colb & 15));
+        }
+      }
+      auto kread8 = [&](int st, int jt, int m, bool lo) __attribute__((always_inline)) -> OpE {
+        const char* b = smem + st * C::STAGE + (lo ? C::LOOFF : 0) + jt * 32 * C::ROWB;  // st: 0 or 1
+        const uint4 a0 = *(const uint4*)(b + ka[2 * m]);
+        const uint4 a1 = *(const uint4*)(b + ka[2 * m + 1]);
+        OpE r = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+        return r;
+      };
+      auto vread8 = [&](int st, int nt) __attribute__((always_inline)) -> OpE {
+        const char* b = smem + st * C::STAGE + va[nt];
+        OpE r;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const i32x2 w = lds_tr8(b + tt * 16 * C::ROWB);
+          r[2 * tt] = w[0];
+          r[2 * tt + 1] = w[1];
+        }
+        return r;
+      };
+      // buffer resource and per-row mode of step it's K/V tile (bases kb/vb),
+      // or of a chunk of pooled means (base mb)
+      auto step_rsrc = [&](int it, int p, const char* base, const char* mb, bool& rows) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+        rows = false;
+        if (it >= T) {
+          const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
+          return make_rsrc(mb + o, mbytes > o ? mbytes - o : 0);
+        }
+        const int j0 = p * kTile;
+        if constexpr (AM == kContig) {
+          const uint64_t o = (uint64_t)j0 * rowstride;
+          return make_rsrc(base + o, kvbytes > o ? kvbytes - o : 0);
+        } else if constexpr (AM == kPagedTile) {
+          const int pg = j0 / g.page_size;
+          const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+          int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
+          if (page < 0 || slot0 + kTile > g.num_slots) {
+            err |= kErrPage;
+            slot0 = 0;
+          }
+          const uint64_t o = (uint64_t)slot0 * rowstride;
+          const uint64_t tail = (uint64_t)max(0, c.L - 1 - j0) * rowstride + C::ROWB;
+          return make_rsrc(base + o, min(kvbytes > o ? kvbytes - o : (uint64_t)0, tail));
+        } else {
+          rows = true;
+          return make_rsrc(base, kvbytes);
+        }
+      };
+      // DMA of one 64-row tile (K-side swizzle when isk) into LDS at dst
+      auto dma_rows = [&](bool isk, char* dst, __amdgpu_buffer_rsrc_t r, bool rows, int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qq = 0; qq < C::NDMA; ++qq) {
+          uint32_t off = isk ? dk[qq] : dv[qq];
+          if constexpr (AM == kPagedAny) {
+            if (rows) {
+              // one page-table lookup per row; rows past the request read as zero
+              const int rr = 16 * wave + C::RPI * qq + lane / C::CPR;
+              const int cl = lane % C::CPR;
+              const int j = j0 + rr;
+              off = 0xfffffff0u;
+              if (j < c.L)
+                off = paged_off(g, c, j, rowstride, err) + (uint32_t)((cl ^ (isk ? swz_k<DT>(rr) : swz_v<DT>(rr))) * 16);
+            }
+          }
+          dma16(r, dst + (16 * wave + C::RPI * qq) * C::ROWB, off);
+        }
+      };
+      auto dma_k = [&](int st, int it, int p) __attribute__((always_inline)) {
+        bool rows;
+        const __amdgpu_buffer_rsrc_t r = step_rsrc(it, p, kbase, kmbase, rows);
+        dma_rows(true, smem + st * C::STAGE, r, rows, p * kTile);
+        if (it >= T) {
+          bool r2;
+          const __amdgpu_buffer_rsrc_t rl = step_rsrc(it, p, kbase, klmbase, r2);
+          dma_rows(true, smem + st * C::STAGE + C::LOOFF, rl, false, 0);
+        }
+      };
+      auto dma_v = [&](int st, int it, int p) __attribute__((always_inline)) {
+        bool rows;
+        const __amdgpu_buffer_rsrc_t r = step_rsrc(it, p, vbase, vmbase, rows);
+        dma_rows(false, smem + st * C::STAGE + C::KBYTES, r, rows, p * kTile);
+      };
+      // correction offsets of step it into table ts (wave 0): +7 where the block
+      // is corrected, -inf where it is selected or not fully visible
+      auto pen3 = [&](int ts, int it) __attribute__((always_inline)) {
+        if (it >= T && tid < 64) {
+          float* pen = (float*)(smem + PEN3 + ts * 256);
+          const int h = tid >> 5, kk = tid & 31;
+          const int rho = 32 * (kk >> 4) + 8 * ((kk & 15) >> 2) + 4 * h + (kk & 3);
+          const int J = (it - T) * kChunk + rho;
+          const bool ok = J < t.beta && !((selbits[J >> 5] >> (J & 31)) & 1u);
+          pen[tid] = ok ? 7.f : -INFINITY;
+        }
+      };
+
+      f32x16 S[2];          // logits of the current step (keys 0-31, 32-63)
+      OpE P = {};           // E4M3 probabilities of the previous step, then of the current one
+      // QK of step it into S (K, and for a correction chunk its lo part, from stage st)
+      auto qk = [&](int st, int it) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          S[jt] = f32x16{};
+#pragma unroll
+          for (int m = 0; m < 2; ++m) S[jt] = mma<DT>(kread8(st, jt, m, false), qf[m], S[jt]);
+        }
+        if (it >= T) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) S[jt] = mma_lo8(kread8(st, jt, m, true), qf[m], S[jt]);
+        }
+      };
+      int cur = next_step(it0);
+      if (cur < it1) {
+        int cur_tile = cur < T ? tile_of(cur) : 0;
+        int nxt = next_step(cur + 1);
+        int nxt_tile = nxt < it1 && nxt < T ? tile_of(nxt) : 0;
+        int ts = 0;  // table of the current step
+        // prologue: K(s0) -> stage 0, K(s1) -> stage 1, V(s0) -> stage 1 (PV of
+        // iteration 0 multiplies it by P = 0: exact zeros); logits of s0
+        dma_k(0, cur, cur_tile);
+        pen3(0, cur);
+        if (nxt < it1) {
+          dma_k(1, nxt, nxt_tile);
+          pen3(1, nxt);
+        }
+        dma_v(1, cur, cur_tile);
+        wait_vmem();
+        __syncthreads();
+        qk(0, cur);
+        __syncthreads();  // every wave has read stage 0's K before iteration 0 refills it
+
+        int par = 1;       // stage the iteration reads: (k + 1) % 2
+        bool first = true;
+        float resc = 1.f;
+        bool need = false;
+        // one iteration, reading stage PAR and filling the other; P holds the
+        // previous step's probabilities until the five MFMAs that read them have
+        // issued, then the current step's
+        auto iter = [&]() __attribute__((always_inline)) {
+          const int PAR = par;
+          const int WR = 1 - PAR;  // stage the DMA fills
+          // the step after next, and this iteration's DMA: K(s_{k+2}) and V(s_k)
+          int nxt2 = nxt, nxt2_tile = 0;
+          if (nxt < it1) {
+            nxt2 = next_step(nxt + 1);
+            if (nxt2 < it1 && nxt2 < T) nxt2_tile = tile_of(nxt2);
+          }
+          const int ts2 = ts == 0 ? 2 : ts - 1;  // (ts + 2) % 3
+          if (nxt2 < it1) {
+            dma_k(WR, nxt2, nxt2_tile);
+            pen3(ts2, nxt2);
+          }
+          dma_v(WR, cur, cur_tile);
+          const bool chunk = cur >= T;
+          // logits in log2 units are S * slk: a tile step holds raw dot products,
+          // a correction step gets its scale and offset (+7, or -inf where masked)
+          // applied here; keys past a row's position are masked here
+          const float slk = chunk ? 1.f : sl;
+          if (chunk) {
+            const f32x4* penp = (const f32x4*)(smem + PEN3 + ts * 256) + half * 8;
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 pv = penp[jt * 4 + r4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[jt][4 * r4 + e] = fmaf(S[jt][4 * r4 + e], sl, pv[e]);
+              }
+          } else if (cur_tile * kTile + kTile - 1 > t.t0) {
+            const int lim = pos - cur_tile * kTile - 4 * half;  // key j visible iff j <= pos - 64 p
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (32 * jt + 8 * (r >> 2) + (r & 3) > lim) S[jt][r] = -INFINITY;
+          }
+          float mrow = 0.f;  // the row maximum of the step's logits
+          float m_use = 0.f;
+          auto piece = [&](int k) __attribute__((always_inline)) {
+            if (k == 0) {
+              float a = fmaxf(S[0][0], fmaxf(S[0][1], S[0][2]));
+              float b = fmaxf(S[1][0], fmaxf(S[1][1], S[1][2]));
+#pragma unroll
+              for (int r = 3; r < 15; r += 2) {
+                a = fmaxf(a, fmaxf(S[0][r], S[0][r + 1]));
+                b = fmaxf(b, fmaxf(S[1][r], S[1][r + 1]));
+              }
+              a = fmaxf(a, fmaxf(S[0][15], b));
+              mrow = fmaxf(S[1][15], a);
+              pin(mrow);
+            } else if (k == 1) {
+              // Eq. 15: the running maximum after this step's logits (slk > 0)
+              const float m_step = max_halves(mrow) * slk;
+              const float m_new = first ? m_step : fmaxf(m_i, m_step);
+              resc = first ? 1.f : __builtin_amdgcn_exp2f(m_i - (m_new == -INFINITY ? 0.f : m_new));
+              need = !first && __any(m_new > m_i);
+              m_i = m_new;
+              m_use = m_i == -INFINITY ? 0.f : m_i;
+              pin(m_use);
+            } else if (k < 6) {
+              const int jt = (k - 2) >> 1, r0 = ((k - 2) & 1) * 8;
+#pragma unroll
+              for (int r = r0; r < r0 + 8; ++r) S[jt][r] = __builtin_amdgcn_exp2f(fmaf(S[jt][r], slk, kOff - m_use));
+#pragma unroll
+              for (int r = r0; r < r0 + 8; ++r) pin(S[jt][r]);
+            } else {
+              const int w0 = (k - 6) * 4;
+#pragma unroll
+              for (int w = w0; w < w0 + 4; ++w) {
+                const int jt = w >> 2, r = (w & 3) * 4;
+                P[w] = (int)f32x4_to_e4m3x4(S[jt][r], S[jt][r + 1], S[jt][r + 2], S[jt][r + 3]);
+              }
+#pragma unroll
+              for (int w = w0; w < w0 + 4; ++w) pin(P[w]);
+            }
+          };
+          // PV(s_{k-1}): its row sums and four output tiles, one softmax piece
+          // after each MFMA (two after the last); the conversion pieces, which
+          // overwrite P, come after all five have issued
+          OpE ring[2];
+          auto fetch = [&](int sl2) __attribute__((always_inline)) -> OpE {
+            return sl2 == 0 ? ones : vread8(PAR, sl2 - 1);
+          };
+          ring[0] = fetch(0);
+          ring[1] = fetch(1);
+#pragma unroll
+          for (int sl2 = 0; sl2 < 5; ++sl2) {
+            const OpE a = ring[sl2 & 1];
+            if (sl2 + 2 < 5) ring[sl2 & 1] = fetch(sl2 + 2);
+            if (sl2 == 0) {
+              lacc = mma<DT>(a, P, lacc);
+              hold(lacc);
+            } else {
+              oacc[sl2 - 1] = mma<DT>(a, P, oacc[sl2 - 1]);
+              hold(oacc[sl2 - 1]);
+            }
+            piece(sl2);
+            if (sl2 == 4) piece(5);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          piece(6);
+          piece(7);
+          // the raised maximum rescales the sums of every earlier step
+          if (need) {
+            lacc[0] *= resc;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
+          }
+          // logits of the next step (its K tile is in the stage read here)
+          if (nxt < it1) qk(PAR, nxt);
+          first = false;
+          wait_vmem();
+          __syncthreads();
+          ts = ts == 2 ? 0 : ts + 1;
+          cur = nxt;
+          cur_tile = nxt_tile;
+          nxt = nxt2;
+          nxt_tile = nxt2_tile;
+        };
+        // steps in order (listed tiles, then correction chunks)
+        while (cur < it1) {
+          iter();
+          par ^= 1;
+        }
+        // PV of the last step: its V tile sits in the stage the last iteration
+        // filled, which par now names
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) oacc[nt] = mma<DT>(vread8(par, nt), P, oacc[nt]);
+        lacc = mma<DT>(ones, P, lacc);
+      }
+      l_i = half ? 0.f : lacc[0];
+    } else {
     // ---- mainloop: loads for step n+1 are in flight while step n computes.
     // Three kinds of step, each run by a loop of its own so that no step pays
     // for another kind's work: listed tiles that reach past the first row's
@@ -1383,6 +1708,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     }
     // e4m3: the complete row sum sits in both lane halves; the epilogue adds halves
     if constexpr (DT == kE4M3) l_i = half ? 0.f : lacc[0];
+    }
 
     }
 
