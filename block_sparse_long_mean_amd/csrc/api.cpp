@@ -130,10 +130,12 @@ fp_status validate_problem(const fp_problem* p, HostGeo* hg) {
   hg->max_len = (int32_t)max_len;
   hg->max_nj = (int32_t)std::max<int64_t>(1, (max_len + kBlock - 1) / kBlock);
   hg->words = (hg->max_nj + 31) / 32 + 1;
-  // K/V rows are addressed through 32-bit buffer ranges (one KV head's rows of
-  // a request, or of the whole page pool), which must stay below 4 GiB
+  // K/V rows are addressed through 32-bit buffer offsets (one KV head's rows of
+  // a request, or of the whole page pool), which must stay below 4 GiB; a
+  // request's last 64-key tile may reach up to 63 rows past its end
   const uint64_t rowstride = (uint64_t)p->num_heads_kv * kD * (p->dtype == FP_F32 ? 4 : p->dtype == FP_BF16 ? 2 : 1);
-  const uint64_t kv_span = (uint64_t)(p->page_table ? std::max<int64_t>(p->num_pool_slots, 1) : max_len) * rowstride;
+  const uint64_t kv_span =
+      (uint64_t)(p->page_table ? std::max<int64_t>(p->num_pool_slots, 1) : max_len + kTile) * rowstride;
   if (kv_span >= 0xfffff000ull)
     return fail(FP_ERR_UNSUPPORTED, "K/V span of %llu bytes per head exceeds the 4 GiB addressing range",
                 (unsigned long long)kv_span);

@@ -156,9 +156,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // read of the stage being computed while the other one fills.  The DMA's
 // completion is made explicit instead: every stage is published by wait_vmem()
 // and a barrier before any wave reads it.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+// The LDS address is a 32-bit integer: a generic pointer cast to LDS costs a
+// 64-bit add and a null test per DMA.  The paged layouts keep the builtin: the
+// compiler may hold their resources in vector registers, which the builtin
+// turns into scalar operands and the assembly form cannot take.
+template <bool ASM>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  if constexpr (ASM) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m0) : "memory");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(uintptr_t)m0, 16, (int)voff, 0, 0, 0);
+  }
 }
 // Transpose reads (see the operand builders below for the lane layout).
 __device__ __forceinline__ i16x4 lds_tr16(const char* p) {
@@ -166,6 +175,20 @@ __device__ __forceinline__ i16x4 lds_tr16(const char* p) {
 }
 __device__ __forceinline__ i32x2 lds_tr8(const char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+// Position of the r-th (from 0) set bit of m; r < popcount(m).
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __builtin_popcountll(m & ((1ull << w) - 1));
+    if (r >= c) {
+      r -= c;
+      m >>= w;
+      pos += w;
+    }
+  }
+  return pos;
 }
 // Wait for this wave's outstanding vector-memory loads (including LDS DMA).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -318,6 +341,14 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   constexpr int KPL = C::KPL;
   constexpr int EB = C::EB;
   extern __shared__ __align__(16) char smem[];
+  // LDS address of smem, and the DMA of 16 bytes per lane to p + 16 * lane
+  // for a pointer p into smem
+  // (held opaque: otherwise the cast's null test is redone at every use)
+  uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)smem);
+  asm volatile("" : "+s"(sb));
+  auto dma = [&](__amdgpu_buffer_rsrc_t r, const char* p, uint32_t voff) __attribute__((always_inline)) {
+    dma16<AM == kContig>(r, sb + (uint32_t)(p - smem), voff);
+  };
   uint32_t* selbits = (uint32_t*)(smem + C::SELOFF);
 
   // the wave index is uniform: in a scalar register, addresses derived from it
@@ -459,12 +490,15 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     const char* vtbase = (const char*)v + (AM == kContig ? (uint64_t)c.h * kD * g.vrow + c.kv0 : 0);
     const char* vtmbase = means + ml.vop + (uint64_t)((ur.blk_base >> 6) * g.hkv + c.h) * kD * kChunk;
     const uint64_t mbytes = (uint64_t)(((t.beta + kChunk - 1) / kChunk) * kChunk) * rowstride;
+    // One buffer resource per operand for the whole unit: the request's K and V
+    // rows of this head (contiguous layout) and its pooled means.  A step adds
+    // its first row's offset to the per-lane offsets; rows of a tile past the
+    // request's last row fall outside the range and read as zero.
+    const __amdgpu_buffer_rsrc_t rk_t = make_rsrc(kbase, kvbytes), rv_t = make_rsrc(vbase, kvbytes);
+    const __amdgpu_buffer_rsrc_t rk_m = make_rsrc(kmbase, mbytes), rv_m = make_rsrc(vmbase, mbytes);
+    const __amdgpu_buffer_rsrc_t rl_m = make_rsrc(klmbase, mbytes);
+    const uint32_t tile_bytes = (uint32_t)kTile * rowstride;  // kChunk == kTile rows
 
-    // listed tiles of the first 64 steps, one per lane (step it reads lane it)
-    int vidx = 0;
-    if constexpr (!DENSE) {
-      if (lane < T) vidx = idx[seg0 + T - 1 - lane];
-    }
     if (NC > 0) {
       for (int w = tid; w <= (t.beta >> 5) + 2; w += 256) selbits[w] = 0;
       __syncthreads();
@@ -523,34 +557,59 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) oacc[nt] = f32x16{};
 
-    // ---- steps: listed tiles backwards (Eq. 17), then correction chunks
-    // the first step at or after it that has work: a listed tile, or a
-    // correction chunk whose bit is set
-    auto next_step = [&](int it) -> int {
-      if (it < T || it >= it1) return it;
-      const int ch = it - T;
-      const uint64_t lo = ch < 64 ? todo_lo & (~0ull << ch) : 0ull;
-      const uint64_t hi = ch < 64 ? todo_hi : ch < 128 ? todo_hi & (~0ull << (ch - 64)) : 0ull;
-      const int nc = lo ? __builtin_ctzll(lo) : hi ? 64 + __builtin_ctzll(hi) : (1 << 20);
-      return min(T + nc, it1);
-    };
-    // strictly ascending list: a split also checks the entry its predecessor saw last
+    // ---- steps: listed tiles backwards (Eq. 17), then the correction chunks
+    // that have work.  The unit's steps are handed out in order from a window
+    // of 64 held one per lane: lane j of w_it is the step index of the
+    // (wb + j)-th step and lane j of w_p its listed tile (0 for a chunk); past
+    // the unit's last step the index is it1.  Each wave fills its window
+    // itself when the previous one is used up, and checks the listed tiles
+    // there: descending (the list is strictly ascending) and inside the rows'
+    // visible keys; a split also checks the entry its predecessor saw last.
+    const int nt = max(0, min(it1, T) - it0);         // tile steps of the unit
+    const int c_lo = max(it0, T) - T, c_hi = it1 - T;  // its chunk range
+    uint64_t cm_lo = 0, cm_hi = 0;                     // chunks with work in it
+    if (NC > 0) {
+      cm_lo = __ballot(((todo_lo >> lane) & 1) && lane >= c_lo && lane < c_hi);
+      cm_hi = __ballot(((todo_hi >> lane) & 1) && lane + 64 >= c_lo && lane + 64 < c_hi);
+    }
+    const int n1 = __builtin_popcountll(cm_lo);
+    const int nsteps = nt + n1 + __builtin_popcountll(cm_hi);
     int prev_tile = 1 << 30;
     if constexpr (!DENSE) {
       if (it0 > 0 && it0 < T) prev_tile = idx[seg0 + T - it0];
     }
-    auto tile_of = [&](int it) -> int {
-      if constexpr (DENSE) {
-        return T - 1 - it;
-      } else {
-        int p = it < 64 ? __builtin_amdgcn_readlane(vidx, it) : __builtin_amdgcn_readfirstlane(idx[seg0 + T - 1 - it]);
-        if (p < 0 || (int64_t)p * kTile > t.t1 || p >= prev_tile) {
-          err |= kErrIdx;
-          p = 0;
+    int w_it = it1, w_p = 0, wb = -64, rd = 0;
+    auto fill = [&]() {
+      wb += 64;
+      const int k = wb + lane;
+      int e_it = it1, e_p = 0;
+      if (k < nt) {
+        e_it = it0 + k;
+        if constexpr (DENSE) {
+          e_p = T - 1 - e_it;
+        } else {
+          e_p = idx[seg0 + T - 1 - e_it];
         }
-        prev_tile = p;
-        return p;
+      } else if (k < nsteps) {
+        // the chunk of rank r among those with work is step nt + r
+        const int r = k - nt;
+        e_it = T + (r < n1 ? nth_set_bit(cm_lo, r) : 64 + nth_set_bit(cm_hi, r - n1));
       }
+      if constexpr (!DENSE) {
+        const int before = __builtin_amdgcn_ds_bpermute(((lane + 63) & 63) * 4, e_p);
+        const bool bad = k < nt && (e_p < 0 || (int64_t)e_p * kTile > t.t1 || e_p >= (lane == 0 ? prev_tile : before));
+        if (__ballot(bad)) err |= kErrIdx;
+        prev_tile = __builtin_amdgcn_readlane(e_p, 63);
+        if (bad) e_p = 0;
+      }
+      w_it = e_it;
+      w_p = e_p;
+    };
+    auto pop = [&](int& it, int& p) __attribute__((always_inline)) {
+      if (rd - wb == 64) fill();
+      it = __builtin_amdgcn_readlane(w_it, rd - wb);
+      p = __builtin_amdgcn_readlane(w_p, rd - wb);
+      ++rd;
     };
 
     // One-step paths (e4m3, fp32): output rescaling is deferred until a row's
@@ -591,22 +650,19 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         constexpr bool ISK = decltype(isk_tag)::value;
         constexpr int NQ = ISK ? PL::NK : PL::NV, SPR = ISK ? PL::KSL : PL::VSL;
         const char* base = ISK ? kbase : vbase;
-        const char* mb = ISK ? kmbase : vmbase;
         __amdgpu_buffer_rsrc_t r;
+        uint32_t soff = 0;  // the step's first row within r
         bool rows = false;
         int j0 = 0;
         if (it < T) {
           j0 = p * kTile;
           if constexpr (AM == kContig) {
-            // bytes from the tile's first row to the end of the request's last
-            // row, or no limit when the whole tile lies inside the request
-            const int rem = c.L - 1 - j0;
-            const uint32_t n = rem >= kTile ? 0xffffffffu : rem < 0 ? 0u : (uint32_t)rem * rowstride + kD * EB;
-            r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base) + (uint64_t)j0 * rowstride, (short)0,
-                                                  (int)n, kBufFlags);
+            r = ISK ? rk_t : rv_t;
+            soff = (uint32_t)p * tile_bytes;
           } else if constexpr (AM == kPagedTile) {
             const int pg = j0 / g.page_size;
-            const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+            // one page for the whole tile: its number is wave-uniform (a scalar operand)
+            const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
             int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
             if (page < 0 || slot0 + kTile > g.num_slots) {
               err |= kErrPage;
@@ -621,14 +677,14 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
         } else {
           // a whole chunk of 64 means rows: the means are padded to full chunks
-          const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
-          r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(mb) + o, (short)0, (int)0xffffffffu, kBufFlags);
+          r = ISK ? rk_m : rv_m;
+          soff = (uint32_t)(it - T) * tile_bytes;
         }
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
           const int q = wave + 4 * i;
           if (i < 4 || q < NQ) {
-            uint32_t voff = ISK ? pdk[i] : pdv[i];
+            uint32_t voff = (ISK ? pdk[i] : pdv[i]) + soff;
             if constexpr (AM == kPagedAny) {
               if (rows) {
                 // one page-table lookup per row; rows past the request read as zero
@@ -637,7 +693,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
                 voff = j < c.L ? paged_off(g, c, j, rowstride, err) + (uint32_t)cc * 16 : 0xfffffff0u;
               }
             }
-            dma16(r, smem + lds_off + q * 1024, voff);
+            dma(r, smem + lds_off + q * 1024, voff);
           }
         }
       };
@@ -654,11 +710,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
       };
 
-      int cur = next_step(it0);
+      int cur, cur_tile;
+      pop(cur, cur_tile);
       if (cur < it1) {
-        int cur_tile = cur < T ? tile_of(cur) : 0;
-        int nxt = next_step(cur + 1);
-        int nxt_tile = nxt < it1 && nxt < T ? tile_of(nxt) : 0;
+        int nxt, nxt_tile;
+        pop(nxt, nxt_tile);
         int bk = 0, ps = 0;  // parity of step n; its correction table n % 3
         // prologue: K(0), V(0), K(1) staged; A(0)
         dma_bf16(std::true_type{}, PL::K0, cur, cur_tile);
@@ -825,10 +881,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           wait_vmem();
           __syncthreads();
           int nxt2 = nxt, nxt2_tile = 0;
-          if (nxt < it1) {
-            nxt2 = next_step(nxt + 1);
-            if (nxt2 < it1 && nxt2 < T) nxt2_tile = tile_of(nxt2);
-          }
+          if (nxt < it1) pop(nxt2, nxt2_tile);
           if (nxt2 < it1) {
             dma_bf16(std::true_type{}, bk ? PL::K1 : PL::K0, nxt2, nxt2_tile);
             pen_bf16(ps == 0 ? 2 : ps - 1, nxt2);
@@ -922,7 +975,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) {
         const uint32_t o = means_tile ? dvm[qq] : (j0 + 16 * vt_cs[qq] < c.L ? dvt[qq] : 0xfffffff0u);
-        dma16(rv, vs + 16 * (2 * wave + qq) * 64, o);
+        dma(rv, vs + 16 * (2 * wave + qq) * 64, o);
       }
     };
     Vec8<DT> kst[C::DMA ? 1 : 4], vst[C::DMA ? 1 : 4];
@@ -934,8 +987,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
       for (int qq = 0; qq < C::NDMA; ++qq) {
         const int r0 = 16 * wave + C::RPI * qq;
-        dma16(rk, ks + r0 * C::ROWB, dk[qq]);
-        if constexpr (!VC) dma16(rv, vs + r0 * C::ROWB, dv[qq]);
+        dma(rk, ks + r0 * C::ROWB, dk[qq]);
+        if constexpr (!VC) dma(rv, vs + r0 * C::ROWB, dv[qq]);
       }
     };
     // paged, any page size: one page-table lookup per row; rows past the request
@@ -954,8 +1007,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         const uint32_t ok_k = ok ? ok : base + (uint32_t)((cl ^ swz_k<DT>(r)) * 16);
         const uint32_t ok_v = ok ? ok : base + (uint32_t)((cl ^ swz_v<DT>(r)) * 16);
         const int r0 = 16 * wave + C::RPI * qq;
-        dma16(rk, ks + r0 * C::ROWB, ok_k);
-        dma16(rv, vs + r0 * C::ROWB, ok_v);
+        dma(rk, ks + r0 * C::ROWB, ok_k);
+        dma(rv, vs + r0 * C::ROWB, ok_v);
       }
     };
 
@@ -997,7 +1050,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
         } else if constexpr (AM == kPagedTile) {
           const int pg = j0 / g.page_size;
-          const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+          // one page for the whole tile: its number is wave-uniform (a scalar operand)
+          const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
           int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
           if (page < 0 || slot0 + kTile > g.num_slots) {
             err |= kErrPage;
@@ -1060,7 +1114,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           const __amdgpu_buffer_rsrc_t rl = make_rsrc(klmbase + o, left);
           char* ls = smem + buf * C::STAGE + C::LOOFF;
 #pragma unroll
-          for (int qq = 0; qq < C::NDMA; ++qq) dma16(rl, ls + (16 * wave + C::RPI * qq) * C::ROWB, dk[qq]);
+          for (int qq = 0; qq < C::NDMA; ++qq) dma(rl, ls + (16 * wave + C::RPI * qq) * C::ROWB, dk[qq]);
         }
       }
       if constexpr (C::DMA) write_pen(buf, it);
@@ -1193,21 +1247,25 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
         return r;
       };
-      // buffer resource and per-row mode of step it's K/V tile (bases kb/vb),
-      // or of a chunk of pooled means (base mb)
-      auto step_rsrc = [&](int it, int p, const char* base, const char* mb, bool& rows) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+      // buffer resource, first-row offset and per-row mode of step it's K, V
+      // or K-lo tile: rt for a listed tile (contiguous layout), rm for a chunk
+      // of pooled means; the paged layouts build theirs from base
+      auto step_src = [&](int it, int p, const char* base, __amdgpu_buffer_rsrc_t rt, __amdgpu_buffer_rsrc_t rm,
+                          uint32_t& soff, bool& rows) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
         rows = false;
+        soff = 0;
         if (it >= T) {
-          const uint64_t o = (uint64_t)((it - T) * kChunk) * rowstride;
-          return make_rsrc(mb + o, mbytes > o ? mbytes - o : 0);
+          soff = (uint32_t)(it - T) * tile_bytes;
+          return rm;
         }
         const int j0 = p * kTile;
         if constexpr (AM == kContig) {
-          const uint64_t o = (uint64_t)j0 * rowstride;
-          return make_rsrc(base + o, kvbytes > o ? kvbytes - o : 0);
+          soff = (uint32_t)p * tile_bytes;
+          return rt;
         } else if constexpr (AM == kPagedTile) {
           const int pg = j0 / g.page_size;
-          const int64_t page = g.page_table[(int64_t)c.b * g.max_pages + pg];
+          // one page for the whole tile: its number is wave-uniform (a scalar operand)
+          const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
           int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
           if (page < 0 || slot0 + kTile > g.num_slots) {
             err |= kErrPage;
@@ -1222,10 +1280,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
       };
       // DMA of one 64-row tile (K-side swizzle when isk) into LDS at dst
-      auto dma_rows = [&](bool isk, char* dst, __amdgpu_buffer_rsrc_t r, bool rows, int j0) __attribute__((always_inline)) {
+      auto dma_rows = [&](bool isk, char* dst, __amdgpu_buffer_rsrc_t r, uint32_t soff, bool rows, int j0)
+                          __attribute__((always_inline)) {
 #pragma unroll
         for (int qq = 0; qq < C::NDMA; ++qq) {
-          uint32_t off = isk ? dk[qq] : dv[qq];
+          uint32_t off = (isk ? dk[qq] : dv[qq]) + soff;
           if constexpr (AM == kPagedAny) {
             if (rows) {
               // one page-table lookup per row; rows past the request read as zero
@@ -1237,23 +1296,21 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
                 off = paged_off(g, c, j, rowstride, err) + (uint32_t)((cl ^ (isk ? swz_k<DT>(rr) : swz_v<DT>(rr))) * 16);
             }
           }
-          dma16(r, dst + (16 * wave + C::RPI * qq) * C::ROWB, off);
+          dma(r, dst + (16 * wave + C::RPI * qq) * C::ROWB, off);
         }
       };
       auto dma_k = [&](int st, int it, int p) __attribute__((always_inline)) {
         bool rows;
-        const __amdgpu_buffer_rsrc_t r = step_rsrc(it, p, kbase, kmbase, rows);
-        dma_rows(true, smem + st * C::STAGE, r, rows, p * kTile);
-        if (it >= T) {
-          bool r2;
-          const __amdgpu_buffer_rsrc_t rl = step_rsrc(it, p, kbase, klmbase, r2);
-          dma_rows(true, smem + st * C::STAGE + C::LOOFF, rl, false, 0);
-        }
+        uint32_t soff;
+        const __amdgpu_buffer_rsrc_t r = step_src(it, p, kbase, rk_t, rk_m, soff, rows);
+        dma_rows(true, smem + st * C::STAGE, r, soff, rows, p * kTile);
+        if (it >= T) dma_rows(true, smem + st * C::STAGE + C::LOOFF, rl_m, soff, false, 0);
       };
       auto dma_v = [&](int st, int it, int p) __attribute__((always_inline)) {
         bool rows;
-        const __amdgpu_buffer_rsrc_t r = step_rsrc(it, p, vbase, vmbase, rows);
-        dma_rows(false, smem + st * C::STAGE + C::KBYTES, r, rows, p * kTile);
+        uint32_t soff;
+        const __amdgpu_buffer_rsrc_t r = step_src(it, p, vbase, rv_t, rv_m, soff, rows);
+        dma_rows(false, smem + st * C::STAGE + C::KBYTES, r, soff, rows, p * kTile);
       };
       // correction offsets of step it into table ts (wave 0): +7 where the block
       // is corrected, -inf where it is selected or not fully visible
@@ -1270,26 +1327,43 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 
       f32x16 S[2];          // logits of the current step (keys 0-31, 32-63)
       OpE P = {};           // E4M3 probabilities of the previous step, then of the current one
-      // QK of step it into S (K, and for a correction chunk its lo part, from stage st)
-      auto qk = [&](int st, int it) __attribute__((always_inline)) {
+      // QK of step it into S from stage st, in two parts: qk_read requests the
+      // first two K operands into kr (early, so that their LDS latency passes
+      // under other work), qk_mma issues the MFMAs and reads the other operands
+      // two ahead: 4, or 8 for a correction chunk (hi, then the 2^-4-scaled lo
+      // part).  Operand j: logit tile j % 2, key group (j / 2) % 2, lo if j >= 4,
+      // so that consecutive MFMAs accumulate into different tiles.
+      auto kop = [&](int st, int jj) __attribute__((always_inline)) -> OpE {
+        return kread8(st, jj & 1, (jj >> 1) & 1, jj >= 4);
+      };
+      auto qk_read = [&](int st, OpE* kr) __attribute__((always_inline)) {
+        kr[0] = kop(st, 0);
+        kr[1] = kop(st, 1);
+      };
+      auto qk_mma = [&](int st, int it, OpE* kr) __attribute__((always_inline)) {
+        const bool lo = it >= T;
+        S[0] = f32x16{};
+        S[1] = f32x16{};
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          S[jt] = f32x16{};
-#pragma unroll
-          for (int m = 0; m < 2; ++m) S[jt] = mma<DT>(kread8(st, jt, m, false), qf[m], S[jt]);
+        for (int jj = 0; jj < 4; ++jj) {
+          const OpE a = kr[jj & 1];
+          if (jj < 2 || lo) kr[jj & 1] = kop(st, jj + 2);
+          S[jj & 1] = mma<DT>(a, qf[(jj >> 1) & 1], S[jj & 1]);
         }
-        if (it >= T) {
+        if (lo) {
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) S[jt] = mma_lo8(kread8(st, jt, m, true), qf[m], S[jt]);
+          for (int jj = 4; jj < 8; ++jj) {
+            const OpE a = kr[jj & 1];
+            if (jj < 6) kr[jj & 1] = kop(st, jj + 2);
+            S[jj & 1] = mma_lo8(a, qf[(jj >> 1) & 1], S[jj & 1]);
+          }
         }
       };
-      int cur = next_step(it0);
+      int cur, cur_tile;
+      pop(cur, cur_tile);
       if (cur < it1) {
-        int cur_tile = cur < T ? tile_of(cur) : 0;
-        int nxt = next_step(cur + 1);
-        int nxt_tile = nxt < it1 && nxt < T ? tile_of(nxt) : 0;
+        int nxt, nxt_tile;
+        pop(nxt, nxt_tile);
         int ts = 0;  // table of the current step
         // prologue: K(s0) -> stage 0, K(s1) -> stage 1, V(s0) -> stage 1 (PV of
         // iteration 0 multiplies it by P = 0: exact zeros); logits of s0
@@ -1302,7 +1376,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         dma_v(1, cur, cur_tile);
         wait_vmem();
         __syncthreads();
-        qk(0, cur);
+        {
+          OpE kr[2];
+          qk_read(0, kr);
+          qk_mma(0, cur, kr);
+        }
         __syncthreads();  // every wave has read stage 0's K before iteration 0 refills it
 
         int par = 1;       // stage the iteration reads: (k + 1) % 2
@@ -1317,10 +1395,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           const int WR = 1 - PAR;  // stage the DMA fills
           // the step after next, and this iteration's DMA: K(s_{k+2}) and V(s_k)
           int nxt2 = nxt, nxt2_tile = 0;
-          if (nxt < it1) {
-            nxt2 = next_step(nxt + 1);
-            if (nxt2 < it1 && nxt2 < T) nxt2_tile = tile_of(nxt2);
-          }
+          if (nxt < it1) pop(nxt2, nxt2_tile);
           const int ts2 = ts == 0 ? 2 : ts - 1;  // (ts + 2) % 3
           if (nxt2 < it1) {
             dma_k(WR, nxt2, nxt2_tile);
@@ -1352,6 +1427,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
           float mrow = 0.f;  // the row maximum of the step's logits
           float m_use = 0.f;
+          OpE Pn;  // the step's E4M3 probabilities, two words per exp piece
           auto piece = [&](int k) __attribute__((always_inline)) {
             if (k == 0) {
               float a = fmaxf(S[0][0], fmaxf(S[0][1], S[0][2]));
@@ -1373,49 +1449,66 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               m_i = m_new;
               m_use = m_i == -INFINITY ? 0.f : m_i;
               pin(m_use);
-            } else if (k < 6) {
-              const int jt = (k - 2) >> 1, r0 = ((k - 2) & 1) * 8;
-#pragma unroll
-              for (int r = r0; r < r0 + 8; ++r) S[jt][r] = __builtin_amdgcn_exp2f(fmaf(S[jt][r], slk, kOff - m_use));
-#pragma unroll
-              for (int r = r0; r < r0 + 8; ++r) pin(S[jt][r]);
             } else {
-              const int w0 = (k - 6) * 4;
+              // weights of 8 logits, rounded to E4M3 at once (two words of Pn)
+              const int jt = (k - 2) >> 1, r0 = ((k - 2) & 1) * 8;
+              float e[8];
 #pragma unroll
-              for (int w = w0; w < w0 + 4; ++w) {
-                const int jt = w >> 2, r = (w & 3) * 4;
-                P[w] = (int)f32x4_to_e4m3x4(S[jt][r], S[jt][r + 1], S[jt][r + 2], S[jt][r + 3]);
-              }
-#pragma unroll
-              for (int w = w0; w < w0 + 4; ++w) pin(P[w]);
+              for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(S[jt][r0 + r], slk, kOff - m_use));
+              Pn[jt * 4 + r0 / 4] = (int)f32x4_to_e4m3x4(e[0], e[1], e[2], e[3]);
+              Pn[jt * 4 + r0 / 4 + 1] = (int)f32x4_to_e4m3x4(e[4], e[5], e[6], e[7]);
+              pin(Pn[jt * 4 + r0 / 4]);
+              pin(Pn[jt * 4 + r0 / 4 + 1]);
             }
           };
-          // PV(s_{k-1}): its row sums and four output tiles, one softmax piece
-          // after each MFMA (two after the last); the conversion pieces, which
-          // overwrite P, come after all five have issued
-          OpE ring[2];
+          // MFMA slots: 0 the row sums and 1-4 PV(s_{k-1}) over the old weights
+          // P, then 5-8 QK(s_{k+1}) into S (9-12: the lo part of a correction
+          // chunk).  The softmax pieces of s_k run after slots 0-5; a logit
+          // tile is consumed by two exp pieces before its first QK slot writes
+          // it again.  Operands come through a two-deep ring: V tiles, then K,
+          // read whether or not they are needed (a conditional read would make
+          // the ring a join and its load a wait): after the unit's last step the
+          // QK slots read a stale stage and their logits are never used; a
+          // tile step's ring also brings the first two lo operands.
+          const bool qlo = nxt < it1 && nxt >= T;
           auto fetch = [&](int sl2) __attribute__((always_inline)) -> OpE {
-            return sl2 == 0 ? ones : vread8(PAR, sl2 - 1);
+            return sl2 <= 4 ? vread8(PAR, sl2 - 1) : kop(PAR, sl2 - 5);
           };
-          ring[0] = fetch(0);
+          OpE ring[2];
           ring[1] = fetch(1);
+          ring[0] = fetch(2);
+          lacc = mma<DT>(ones, P, lacc);
+          hold(lacc);
+          piece(0);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int sl2 = 0; sl2 < 5; ++sl2) {
+          for (int sl2 = 1; sl2 <= 8; ++sl2) {
             const OpE a = ring[sl2 & 1];
-            if (sl2 + 2 < 5) ring[sl2 & 1] = fetch(sl2 + 2);
-            if (sl2 == 0) {
-              lacc = mma<DT>(a, P, lacc);
-              hold(lacc);
-            } else {
+            ring[sl2 & 1] = fetch(sl2 + 2);
+            if (sl2 <= 4) {
               oacc[sl2 - 1] = mma<DT>(a, P, oacc[sl2 - 1]);
               hold(oacc[sl2 - 1]);
+              piece(sl2);
+            } else {
+              const int jt = (sl2 - 5) & 1, m = (sl2 - 5) >> 1;
+              S[jt] = mma<DT>(a, qf[m], m == 0 ? f32x16{} : S[jt]);
+              hold(S[jt]);
+              if (sl2 == 5) piece(5);
             }
-            piece(sl2);
-            if (sl2 == 4) piece(5);
             __builtin_amdgcn_sched_barrier(0);
           }
-          piece(6);
-          piece(7);
+          if (qlo) {
+#pragma unroll
+            for (int sl2 = 9; sl2 <= 12; ++sl2) {
+              const OpE a = ring[sl2 & 1];
+              if (sl2 + 2 <= 12) ring[sl2 & 1] = fetch(sl2 + 2);
+              const int jt = (sl2 - 9) & 1, m = (sl2 - 9) >> 1;
+              S[jt] = mma_lo8(a, qf[m], S[jt]);
+              hold(S[jt]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          P = Pn;
           // the raised maximum rescales the sums of every earlier step
           if (need) {
             lacc[0] *= resc;
@@ -1424,8 +1517,6 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
               for (int r = 0; r < 16; ++r) oacc[nt][r] *= resc;
           }
-          // logits of the next step (its K tile is in the stage read here)
-          if (nxt < it1) qk(PAR, nxt);
           first = false;
           wait_vmem();
           __syncthreads();
@@ -1454,11 +1545,10 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     // position (causal mask), then the other listed tiles, then correction
     // chunks.  The listed tiles are visited in descending order, so the masked
     // ones come first.
-    int cur = next_step(it0);
+    int cur, cur_tile;
+    pop(cur, cur_tile);
     int buf = 0;
-    int cur_tile = 0;
     if (cur < it1) {
-      cur_tile = cur < T ? tile_of(cur) : 0;
       load_step(0, cur, cur_tile);
       store_step(0, cur);
     }
@@ -1467,12 +1557,9 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 
     auto run_step = [&](auto kind_tag) {
       constexpr int KIND = decltype(kind_tag)::value;  // 0 masked tile, 1 tile, 2 correction chunk
-      const int nxt = next_step(cur + 1);
-      int nxt_tile = 0;
-      if (nxt < it1) {
-        nxt_tile = nxt < T ? tile_of(nxt) : 0;
-        load_step(buf ^ 1, nxt, nxt_tile);
-      }
+      int nxt, nxt_tile;
+      pop(nxt, nxt_tile);
+      if (nxt < it1) load_step(buf ^ 1, nxt, nxt_tile);
       const char* ks = smem + buf * C::STAGE;
       const char* vt = ks + C::KBYTES;
 
