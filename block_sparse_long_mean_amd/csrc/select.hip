@@ -82,52 +82,86 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
   // logits of the 128 rows x 32 blocks whose operands are loaded (block J for
   // this lane's column), 32 rows at a time; per block the running maximum of
   // the raw products (sl > 0) and the sum of 2^(logit - max), logits in log2
-  // units; EXACT uses kbar = hi + lo, otherwise hi alone
+  // units; EXACT uses kbar = hi + lo, otherwise hi alone.  Software-pipelined
+  // over the four row tiles: the MFMAs of row tile rt (into one of two
+  // accumulators) are issued with the statistics of row tile rt - 1 in eight
+  // pieces between them, and the A operands (Q rows) are read two ahead.
   auto tile = [&](auto ragged_tag, auto exact_tag, int J, bool store, const bf16x8 (&bh)[8],
                   const bf16x8 (&bl)[8]) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
     constexpr bool EXACT = decltype(exact_tag)::value;
     float m = -INFINITY, sum = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x16 acc = f32x16{};
-      const uint16_t* arow = qh + (rt * 32 + col) * kQPitch + 8 * half;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 a = *(const bf16x8*)(arow + ks * 16);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], acc, 0, 0, 0);
-        if constexpr (EXACT) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], acc, 0, 0, 0);
-          if constexpr (NQ == 2) {
-            bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], acc, 0, 0, 0);
-          }
+    auto qa = [&](int rt, int ks) __attribute__((always_inline)) -> bf16x8 {
+      return *(const bf16x8*)(qh + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
+    };
+    auto mm = [&](int rt, int ks, const bf16x8 a, f32x16& ac) __attribute__((always_inline)) {
+      ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh[ks], ks == 0 ? f32x16{} : ac, 0, 0, 0);
+      if constexpr (EXACT) {
+        ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl[ks], ac, 0, 0, 0);
+        if constexpr (NQ == 2) {
+          const bf16x8 al = *(const bf16x8*)(ql + (rt * 32 + col) * kQPitch + 8 * half + ks * 16);
+          ac = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh[ks], ac, 0, 0, 0);
         }
       }
-      // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4; padding
-      // rows of a ragged tile are masked out
-      if constexpr (RAGGED) {
+    };
+    // statistics of row tile rt (logits v), piece k of 8: the maximum, the
+    // rescale of the running sum, then 16 weights (two sums)
+    float mn = 0.f, msl = 0.f, s0 = 0.f, s1 = 0.f;
+    auto stat = [&](int rt, f32x16& v, int k) __attribute__((always_inline)) {
+      if (k == 0) {
+        // lane owns block column col, rows rt*32 + 8*(r/4) + 4*half + r%4;
+        // padding rows of a ragged tile are masked out
+        if constexpr (RAGGED) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) acc[r] = -INFINITY;
-      }
-      float m0 = fmaxf(acc[0], fmaxf(acc[1], acc[2])), m1 = fmaxf(acc[8], fmaxf(acc[9], acc[10]));
-      m0 = fmaxf(m0, fmaxf(acc[3], acc[4]));
-      m1 = fmaxf(m1, fmaxf(acc[11], acc[12]));
-      m0 = fmaxf(m0, fmaxf(acc[5], acc[6]));
-      m1 = fmaxf(m1, fmaxf(acc[13], acc[14]));
-      m0 = fmaxf(m0, fmaxf(acc[7], acc[15]));
-      const float mn = fmaxf(m, fmaxf(m0, m1));
-      const float msl = mn == -INFINITY ? 0.f : mn * sl;
-      float s0 = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -msl)), s1 = 0.f;
+          for (int r = 0; r < 16; ++r)
+            if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) v[r] = -INFINITY;
+        }
+        float m0 = fmaxf(v[0], fmaxf(v[1], v[2])), m1 = fmaxf(v[8], fmaxf(v[9], v[10]));
+        m0 = fmaxf(m0, fmaxf(v[3], v[4]));
+        m1 = fmaxf(m1, fmaxf(v[11], v[12]));
+        m0 = fmaxf(m0, fmaxf(v[5], v[6]));
+        m1 = fmaxf(m1, fmaxf(v[13], v[14]));
+        m0 = fmaxf(m0, fmaxf(v[7], v[15]));
+        mn = fmaxf(m, fmaxf(m0, m1));
+        msl = mn == -INFINITY ? 0.f : mn * sl;
+      } else if (k == 1) {
+        s0 = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -msl));
+        s1 = 0.f;
+      } else {
+        // pieces 2-7: weights 0-2, 3-5, 6-8, 9-11, 12-13, 14-15
+        const int r0 = k < 6 ? 3 * (k - 2) : 12 + 2 * (k - 6), r1 = k < 6 ? r0 + 3 : r0 + 2;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        s0 += __builtin_amdgcn_exp2f(fmaf(acc[r], sl, -msl));
-        s1 += __builtin_amdgcn_exp2f(fmaf(acc[r + 1], sl, -msl));
+        for (int r = r0; r < r1; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(v[r], sl, -msl));
+          if (r & 1)
+            s1 += e;
+          else
+            s0 += e;
+        }
+        if (k == 7) {
+          sum = s0 + s1;
+          m = mn;
+        }
       }
-      sum = s0 + s1;
-      m = mn;
+    };
+    f32x16 acc[2];
+    bf16x8 ring[2];
+    ring[0] = qa(0, 0);
+    ring[1] = qa(0, 1);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = ring[ks & 1];
+        const int nrt = ks + 2 < 8 ? rt : rt + 1, nks = (ks + 2) & 7;
+        if (nrt < 4) ring[ks & 1] = qa(nrt, nks);
+        mm(rt, ks, a, acc[rt & 1]);
+        if (rt > 0) stat(rt - 1, acc[(rt - 1) & 1], ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) stat(3, acc[1], k);
     // the other lane half holds the block's other 64 rows
     const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(sum, 32, 64);
     const float mx = fmaxf(m, mo) * sl;
