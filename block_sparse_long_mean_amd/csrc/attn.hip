@@ -748,13 +748,18 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         }
 
         // Softmax state.  The weights of a half step are first taken against
-        // the reference maximum mref (the row's running maximum m_i) with no
-        // reduction at all; only when some lane's 16 weights sum above 2^8 (a
-        // new maximum more than that far up, or the first visible key of a row,
-        // for which mref is -1e30 so that every finite weight overflows) does
-        // the wave take the exact maximum of the half, exchange it between the
-        // lane halves, and compute the weights again.  Exact up to rounding:
-        // the weights stay at most 2^8 times their true scale.
+        // the reference mref = m_i, which sits kHead (log2 units) above the
+        // row's running maximum, with no reduction at all; only when some
+        // lane's 16 weights sum above 2^8 (a key more than about kHead + 4 above
+        // the maximum, or the first visible key of a row, for which mref is
+        // -1e30 so that every finite weight overflows) does the wave take the
+        // exact maximum of the half, exchange it between the lane halves, and
+        // compute the weights again against that maximum + kHead.  Exact up to
+        // rounding: the weights stay within [2^-kHead, 2^8] times their true
+        // scale, and the output and LSE use the same reference.  The headroom
+        // makes the recomputation (and the rescale of the accumulators) rare
+        // when a correction chunk's +7 raises the logits.
+        constexpr float kHead = 8.f;
         float mref = -1e30f, resc = 1.f, psum = 0.f;
         bool need = false;
         uint32_t pw[8];  // the half's weights as bf16 pairs
@@ -811,7 +816,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
               for (int r = 1; r < 16; ++r) mh = fmaxf(mh, sv[r]);
               mh = max_halves(mh);  // the other lane half holds the same query row
               const float m_half = KIND == 2 ? mh : mh * sl;  // tile steps hold raw dot products (sl > 0)
-              const float m_new = fmaxf(m_i, m_half);
+              // the new reference sits kHead above the maximum (m_i includes it)
+              const float m_new = fmaxf(m_i, m_half + kHead);
               const float m_use = m_new == -INFINITY ? 0.f : m_new;
               resc = __builtin_amdgcn_exp2f(m_i - m_use);
               m_i = m_new;
