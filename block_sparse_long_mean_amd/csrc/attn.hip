@@ -176,6 +176,12 @@ __device__ __forceinline__ i16x4 lds_tr16(const char* p) {
 __device__ __forceinline__ i32x2 lds_tr8(const char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
 }
+// A wave-uniform read of read-only data through the constant address space,
+// so that it is a scalar load: a vector load would share the vector-memory
+// counter with the LDS DMA in flight, and waiting for it would wait for them.
+__device__ __forceinline__ int32_t scalar_read(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)p;
+}
 // Position of the r-th (from 0) set bit of m; r < popcount(m).
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int r) {
   int pos = 0;
@@ -661,8 +667,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             soff = (uint32_t)p * tile_bytes;
           } else if constexpr (AM == kPagedTile) {
             const int pg = j0 / g.page_size;
-            // one page for the whole tile: its number is wave-uniform (a scalar operand)
-            const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
+            const int64_t page = scalar_read(g.page_table + (int64_t)c.b * g.max_pages + pg);
             int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
             if (page < 0 || slot0 + kTile > g.num_slots) {
               err |= kErrPage;
@@ -677,8 +682,15 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
         } else {
           // a whole chunk of 64 means rows: the means are padded to full chunks
-          r = ISK ? rk_m : rv_m;
-          soff = (uint32_t)(it - T) * tile_bytes;
+          // (the paged layouts build the resource per step: joined with their
+          // tile resources, the per-unit one is taken for a divergent value and
+          // every DMA becomes a loop over the lanes)
+          if constexpr (AM == kContig) {
+            r = ISK ? rk_m : rv_m;
+            soff = (uint32_t)(it - T) * tile_bytes;
+          } else {
+            r = make_rsrc((ISK ? kmbase : vmbase) + (uint64_t)(it - T) * tile_bytes, mbytes);
+          }
         }
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
@@ -1056,8 +1068,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           }
         } else if constexpr (AM == kPagedTile) {
           const int pg = j0 / g.page_size;
-          // one page for the whole tile: its number is wave-uniform (a scalar operand)
-          const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
+          const int64_t page = scalar_read(g.page_table + (int64_t)c.b * g.max_pages + pg);
           int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
           if (page < 0 || slot0 + kTile > g.num_slots) {
             err |= kErrPage;
@@ -1256,13 +1267,20 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       // buffer resource, first-row offset and per-row mode of step it's K, V
       // or K-lo tile: rt for a listed tile (contiguous layout), rm for a chunk
       // of pooled means; the paged layouts build theirs from base
-      auto step_src = [&](int it, int p, const char* base, __amdgpu_buffer_rsrc_t rt, __amdgpu_buffer_rsrc_t rm,
-                          uint32_t& soff, bool& rows) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+      auto step_src = [&](int it, int p, const char* base, const char* mb, __amdgpu_buffer_rsrc_t rt,
+                          __amdgpu_buffer_rsrc_t rm, uint32_t& soff, bool& rows) __attribute__((always_inline))
+          -> __amdgpu_buffer_rsrc_t {
         rows = false;
         soff = 0;
         if (it >= T) {
-          soff = (uint32_t)(it - T) * tile_bytes;
-          return rm;
+          if constexpr (AM == kContig) {
+            soff = (uint32_t)(it - T) * tile_bytes;
+            return rm;
+          } else {
+            // per step for the paged layouts (a join with their tile resources
+            // would make the per-unit one divergent for the compiler)
+            return make_rsrc(mb + (uint64_t)(it - T) * tile_bytes, mbytes);
+          }
         }
         const int j0 = p * kTile;
         if constexpr (AM == kContig) {
@@ -1270,8 +1288,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           return rt;
         } else if constexpr (AM == kPagedTile) {
           const int pg = j0 / g.page_size;
-          // one page for the whole tile: its number is wave-uniform (a scalar operand)
-          const int64_t page = __builtin_amdgcn_readfirstlane(g.page_table[(int64_t)c.b * g.max_pages + pg]);
+          const int64_t page = scalar_read(g.page_table + (int64_t)c.b * g.max_pages + pg);
           int64_t slot0 = page * g.page_size + (j0 - pg * g.page_size);
           if (page < 0 || slot0 + kTile > g.num_slots) {
             err |= kErrPage;
@@ -1308,14 +1325,19 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
       auto dma_k = [&](int st, int it, int p) __attribute__((always_inline)) {
         bool rows;
         uint32_t soff;
-        const __amdgpu_buffer_rsrc_t r = step_src(it, p, kbase, rk_t, rk_m, soff, rows);
+        const __amdgpu_buffer_rsrc_t r = step_src(it, p, kbase, kmbase, rk_t, rk_m, soff, rows);
         dma_rows(true, smem + st * C::STAGE, r, soff, rows, p * kTile);
-        if (it >= T) dma_rows(true, smem + st * C::STAGE + C::LOOFF, rl_m, soff, false, 0);
+        if (it >= T) {
+          uint32_t soff2;
+          bool rows2;
+          const __amdgpu_buffer_rsrc_t rl = step_src(it, p, kbase, klmbase, rk_t, rl_m, soff2, rows2);
+          dma_rows(true, smem + st * C::STAGE + C::LOOFF, rl, soff2, false, 0);
+        }
       };
       auto dma_v = [&](int st, int it, int p) __attribute__((always_inline)) {
         bool rows;
         uint32_t soff;
-        const __amdgpu_buffer_rsrc_t r = step_src(it, p, vbase, rv_t, rv_m, soff, rows);
+        const __amdgpu_buffer_rsrc_t r = step_src(it, p, vbase, vmbase, rv_t, rv_m, soff, rows);
         dma_rows(false, smem + st * C::STAGE + C::KBYTES, r, soff, rows, p * kTile);
       };
       // correction offsets of step it into table ts (wave 0): +7 where the block
