@@ -360,6 +360,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   // the wave index is uniform: in a scalar register, addresses derived from it
   // (LDS DMA destinations) need no per-instruction readfirstlane
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // this wave's LDS base of the DMA destinations: the bf16 tiles' 1 KB pieces
+  // wave + 4 i, the e4m3 tiles' rows 16 wave + ...; then a stage offset and an
+  // immediate per DMA (held opaque, like sb)
+  uint32_t sb_w1k = sb + (uint32_t)wave * 1024u, sb_wrow = sb + (uint32_t)(16 * wave * C::ROWB);
+  asm volatile("" : "+s"(sb_w1k), "+s"(sb_wrow));
   const int half = lane >> 5, col = lane & 31;
   const UnitRec* units = (const UnitRec*)(ws + wl.units);
   // logits in log2 units: x = s * sl (+ 7 for a mean that stands for 128 keys)
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
                 voff = j < c.L ? paged_off(g, c, j, rowstride, err) + (uint32_t)cc * 16 : 0xfffffff0u;
               }
             }
-            dma(r, smem + lds_off + q * 1024, voff);
+            dma16<AM == kContig>(r, sb_w1k + (uint32_t)lds_off + 4096u * i, voff);
           }
         }
       };
@@ -1319,7 +1324,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
                 off = paged_off(g, c, j, rowstride, err) + (uint32_t)((cl ^ (isk ? swz_k<DT>(rr) : swz_v<DT>(rr))) * 16);
             }
           }
-          dma(r, dst + (16 * wave + C::RPI * qq) * C::ROWB, off);
+          dma16<AM == kContig>(r, sb_wrow + (uint32_t)(dst - smem) + (uint32_t)(C::RPI * qq * C::ROWB), off);
         }
       };
       auto dma_k = [&](int st, int it, int p) __attribute__((always_inline)) {
