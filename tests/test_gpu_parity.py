@@ -250,9 +250,10 @@ def test_longest_request():
 @pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
 def test_long_tile_lists(dtype):
     """alpha = 0 keeps every causal block, so late tiles list more than 64 tiles:
-    the attention kernel holds the list of a unit's first 64 steps in a register
-    and reads longer lists from memory.  Both parts are checked against the
-    oracle on the segments with the longest lists, and against dense attention."""
+    the attention kernel hands a unit's steps out of 64-entry windows and
+    refills the window from the list as it goes.  The segments with the longest
+    lists are checked against the oracle, and the whole output against dense
+    attention."""
     b = _small(dtype, lengths=(6000, 4100), seed=17)
     _print_case("long tile lists", dtype=dtype)
     run = GpuRun(b, alpha=0.0, sink=2, win=4)
