@@ -272,3 +272,35 @@ def test_long_tile_lists(dtype):
         diff = (s_out.float() - d_out.float()).abs()
         assert float(diff.max()) < 1e-2 and float(diff.mean()) < 1e-4
     assert run.device_error() == 0
+
+
+@pytest.mark.parametrize("dtype,page_size", [("e4m3", 64), ("e4m3", 48), ("bf16", 48)])
+def test_paged_long_lists_bitwise(dtype, page_size):
+    """Paged K/V (Eq. 22) on lists longer than one 64-entry step window, with
+    the chunk corrections on and off: every tile is looked up through the page
+    table, and the output must equal the contiguous run bit for bit.  The
+    longest paged segments are also checked against the oracle."""
+    b = _small(dtype, lengths=(6000, 4100), seed=17)
+    _print_case("paged long lists", dtype=dtype, page_size=page_size)
+    pg = synth.page_kv(b, page_size, seed=11)
+    run_c = GpuRun(b, alpha=0.0, sink=2, win=4)
+    run_p = GpuRun(b, paged=pg, alpha=0.0, sink=2, win=4)
+    cu_c, idx_c = run_c.select()
+    cu, idx = run_p.select()
+    np.testing.assert_array_equal(cu_c, cu)
+    np.testing.assert_array_equal(idx_c, idx)
+    sizes = np.diff(cu)
+    assert sizes.max() > 64, int(sizes.max())
+    for corr in (True, False):
+        o_c, l_c = run_c.attn(correction=corr)
+        o_p, l_p = run_p.attn(correction=corr)
+        assert torch.isfinite(o_p.float()).all()
+        assert torch.equal(o_c, o_p) and torch.equal(l_c, l_p)
+    P = oracle_for(run_p)
+    segs = sorted(set(np.argsort(sizes)[-6:].tolist()))
+    out, lse = run_p.attn(correction=True)
+    check_rows(run_p, P, out, lse, segs, cu, idx, correction=True)
+    o_c, _ = run_c.attn(dense=True)
+    o_p, _ = run_p.attn(dense=True)
+    assert torch.equal(o_c, o_p)
+    assert run_c.device_error() == 0 and run_p.device_error() == 0
