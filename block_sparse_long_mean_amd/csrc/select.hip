@@ -144,6 +144,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
         }
       }
     };
+    // hi alone: the lane's reference c (log2 units) is the maximum of its 16
+    // rows in row tile 0 and stays fixed for the other 48 rows, so those need
+    // no maximum and no rescale.  A later row that exceeds c by more than the
+    // fp32 range makes the sum infinite, which the caller detects (the segment
+    // is then scored again with hi + lo).  Terms more than 126 below c, which
+    // underflow, are below 2^-126 of the sum (>= 1, from the row that set c).
+    float cref = 0.f, cmax = -INFINITY;
+    auto stat_hi = [&](int rt, f32x16& v, int k) __attribute__((always_inline)) {
+      if (RAGGED && k == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) v[r] = -INFINITY;
+      }
+      if (rt == 0 && k == 0) {
+        float m0 = fmaxf(v[0], fmaxf(v[1], v[2])), m1 = fmaxf(v[8], fmaxf(v[9], v[10]));
+        m0 = fmaxf(m0, fmaxf(v[3], v[4]));
+        m1 = fmaxf(m1, fmaxf(v[11], v[12]));
+        m0 = fmaxf(m0, fmaxf(v[5], v[6]));
+        m1 = fmaxf(m1, fmaxf(v[13], v[14]));
+        m0 = fmaxf(m0, fmaxf(v[7], v[15]));
+        const float mm0 = fmaxf(m0, m1);
+        cmax = mm0 * sl;
+        cref = mm0 == -INFINITY ? 0.f : cmax;
+        return;
+      }
+      // row tile 0 spreads its 16 weights over pieces 1-7 (the last takes
+      // four), the others two per piece over 0-7
+      const int r0 = rt == 0 ? 2 * k - 2 : 2 * k;
+      const int r1 = rt == 0 ? (k == 7 ? 16 : 2 * k) : 2 * k + 2;
+#pragma unroll
+      for (int r = r0; r < r1; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(v[r], sl, -cref));
+        if (r & 1)
+          s1 += e;
+        else
+          s0 += e;
+      }
+    };
+    auto st = [&](int rt, f32x16& v, int k) __attribute__((always_inline)) {
+      if constexpr (EXACT)
+        stat(rt, v, k);
+      else
+        stat_hi(rt, v, k);
+    };
     f32x16 acc[2];
     bf16x8 ring[2];
     ring[0] = qa(0, 0);
@@ -156,19 +200,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
         const int nrt = ks + 2 < 8 ? rt : rt + 1, nks = (ks + 2) & 7;
         if (nrt < 4) ring[ks & 1] = qa(nrt, nks);
         mm(rt, ks, a, acc[rt & 1]);
-        if (rt > 0) stat(rt - 1, acc[(rt - 1) & 1], ks);
+        if (rt > 0) st(rt - 1, acc[(rt - 1) & 1], ks);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) stat(3, acc[1], k);
+    for (int k = 0; k < 8; ++k) st(3, acc[1], k);
     // the other lane half holds the block's other 64 rows
-    const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(sum, 32, 64);
-    const float mx = fmaxf(m, mo) * sl;
-    sum = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -mx)) + so * __builtin_amdgcn_exp2f(fmaf(mo, sl, -mx));
-    if (half == 0 && store) {
-      mJ[J] = mx;
-      SJ[J] = sum;
+    if constexpr (EXACT) {
+      const float mo = __shfl_xor(m, 32, 64), so = __shfl_xor(sum, 32, 64);
+      const float mx = fmaxf(m, mo) * sl;
+      sum = sum * __builtin_amdgcn_exp2f(fmaf(m, sl, -mx)) + so * __builtin_amdgcn_exp2f(fmaf(mo, sl, -mx));
+      if (half == 0 && store) {
+        mJ[J] = mx;
+        SJ[J] = sum;
+      }
+    } else {
+      // row 0 is valid, so half 0's reference is finite; the merged sum is
+      // >= 1 and its log2 is the block's energy in log2 units.  A half's sum
+      // is finite or +inf (never NaN); an infinite one is passed on as
+      // lE = +inf before the merge could form inf * 0
+      const float sm = s0 + s1;
+      const float co = __shfl_xor(cmax, 32, 64), so = __shfl_xor(sm, 32, 64);
+      const float mx = fmaxf(cmax, co);
+      const float tot = sm * __builtin_amdgcn_exp2f(cmax - mx) + so * __builtin_amdgcn_exp2f(co - mx);
+      const bool ovf = sm == INFINITY || so == INFINITY;
+      if (half == 0 && store) mJ[J] = ovf ? INFINITY : mx + __builtin_amdgcn_logf(tot);
     }
   };
   // The sweep multiplies by kbar's hi part alone.  Its logits are off from
@@ -218,83 +275,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
     gm = wave_max(gm);
     if (lane == 0) qred[wave] = gm;  // read after the sweep's barrier
   }
-  auto sweep = [&](auto ragged_tag, auto exact_tag) {
+  // the column tiles of the wave; the first one's operands are already loaded
+  // unless `reload`
+  auto sweep = [&](auto ragged_tag, auto exact_tag, bool reload) {
     for (int jt = wave; jt < njt; jt += 4) {
-      if (jt != wave) kb_load(exact_tag, jt, bh, bl);
+      if (jt != wave || reload) kb_load(exact_tag, jt, bh, bl);
       tile(ragged_tag, exact_tag, jt * 32 + col, jt * 32 + col < nc, bh, bl);
     }
   };
-  if (exact) {
+  auto sweep_exact = [&](bool reload) {
     if (nrows < kRows)
-      sweep(std::true_type{}, std::true_type{});
+      sweep(std::true_type{}, std::true_type{}, reload);
     else
-      sweep(std::false_type{}, std::true_type{});
-  } else {
-    if (nrows < kRows)
-      sweep(std::true_type{}, std::false_type{});
-    else
-      sweep(std::false_type{}, std::false_type{});
-  }
-  __syncthreads();
-
-  // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced.
+      sweep(std::false_type{}, std::true_type{}, reload);
+    __syncthreads();
+  };
   auto forced_block = [&](int J) { return J < sink || (J >= t.beta - win && J < t.beta) || J >= t.beta; };
-  float lm = -INFINITY;
-  for (int J = threadIdx.x; J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
-  const float M = block_max(lm, red);
-  float Emax, thr;
-  if (exact) {
+  // blocks of this thread, J = threadIdx.x + 256 k, with |lo_J|_2
+  auto each_block = [&](auto&& body) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int J = threadIdx.x + 256 * k;
+      if (J < nc) body(J, kb4[k]);
+    }
+    for (int J = threadIdx.x + 1024; J < nc; J += 256) body(J, kbnd[(int64_t)J * g.hkv]);
+  };
+  // The hi-only sweep leaves lE_J = log2 of block J's energy (relative to an
+  // arbitrary common reference) in mJ; its hi + lo value lies in
+  // [lE_J - d_J, lE_J + d_J].  A segment where a sum overflowed is scored
+  // again with hi + lo.
+  bool redo = false;
+  float ehi = 0.f, elo = 0.f, dsc = 0.f, M = 0.f;
+  if (!exact) {
+    if (nrows < kRows)
+      sweep(std::true_type{}, std::false_type{}, false);
+    else
+      sweep(std::false_type{}, std::false_type{}, false);
+    __syncthreads();
+    const float q2 = sqrtf(fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3])) * (1.f + 0.001f));
+    dsc = sl * q2 * (1.f + 0.0078125f);
+    // max lE lies in [elo, ehi]: one two-value workgroup maximum
+    float lhi = -INFINITY, llo = -INFINITY, lmx = -INFINITY;
+    bool ovf = false;
+    each_block([&](int J, float lb) {
+      const float le = mJ[J], d = dsc * lb;
+      if (le == INFINITY) ovf = true;  // a sum overflowed (the tile stores +inf, never NaN)
+      lhi = fmaxf(lhi, le + d);
+      llo = fmaxf(llo, le - d);
+      lmx = fmaxf(lmx, le);
+    });
+    lhi = wave_max(lhi);
+    llo = wave_max(llo);
+    lmx = wave_max(lmx);
+    const bool wovf = __ballot(ovf) != 0;
+    if (lane == 0) {
+      pm[0][wave] = lhi;
+      pm[1][wave] = llo;
+      pm[2][wave] = lmx;
+      nsel_w[wave] = wovf;
+    }
+    if (threadIdx.x == 0) nflag_sh = nunc_sh = 0;
+    __syncthreads();
+    ehi = fmaxf(fmaxf(pm[0][0], pm[0][1]), fmaxf(pm[0][2], pm[0][3]));
+    elo = fmaxf(fmaxf(pm[1][0], pm[1][1]), fmaxf(pm[1][2], pm[1][3]));
+    M = fmaxf(fmaxf(pm[2][0], pm[2][1]), fmaxf(pm[2][2], pm[2][3]));
+    redo = (nsel_w[0] | nsel_w[1] | nsel_w[2] | nsel_w[3]) != 0;
+    if (redo) __syncthreads();  // pm and nsel_w are read before they are written again
+  }
+  if (exact || redo) sweep_exact(redo);
+
+  float thr;
+  if (exact || redo) {
+    // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced
+    float lm = -INFINITY;
+    for (int J = threadIdx.x; J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
+    const float M = block_max(lm, red);
     float le = 0.f;
     for (int J = threadIdx.x; J < nc; J += 256) {
       float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
       SJ[J] = e;
       le = fmaxf(le, e);
     }
-    Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
+    const float Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
     thr = alpha * Emax;
-  } else {
-    // bounds: the hi + lo energy of block J lies in [E_J 2^-d_J, E_J 2^d_J]
-    auto each_block = [&](auto&& body) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int J = threadIdx.x + 256 * k;
-        if (J < nc) body(J, kb4[k]);
-      }
-      for (int J = threadIdx.x + 1024; J < nc; J += 256) body(J, kbnd[(int64_t)J * g.hkv]);
-    };
-    const float q2 = sqrtf(fmaxf(fmaxf(qred[0], qred[1]), fmaxf(qred[2], qred[3])) * (1.f + 0.001f));
-    const float dsc = sl * q2 * (1.f + 0.0078125f);
-    float lhi = 0.f, llo = 0.f;
-    each_block([&](int J, float lb) {
-      const float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
-      const float d = dsc * lb;
-      SJ[J] = e;
-      lhi = fmaxf(lhi, e * __builtin_amdgcn_exp2f(d));
-      llo = fmaxf(llo, e * __builtin_amdgcn_exp2f(-d));
-    });
-    // max E lies in [elo, ehi]: one two-value workgroup maximum
-    lhi = wave_max(lhi);
-    llo = wave_max(llo);
-    if (lane == 0) {
-      pm[0][wave] = lhi;
-      pm[1][wave] = llo;
+    if (energies) {
+      for (int J = threadIdx.x; J < nc; J += 256) energies[s * g.max_nj + J] = SJ[J] / Emax;
+      for (int J = nc + threadIdx.x; J < g.max_nj; J += 256) energies[s * g.max_nj + J] = -1.f;
     }
-    if (threadIdx.x == 0) nflag_sh = nunc_sh = 0;
-    __syncthreads();
-    const float ehi = fmaxf(fmaxf(pm[0][0], pm[0][1]), fmaxf(pm[0][2], pm[0][3]));
-    const float elo = fmaxf(fmaxf(pm[1][0], pm[1][1]), fmaxf(pm[1][2], pm[1][3]));
-    // decided blocks become +inf (kept) or 0 (dropped); the others, and every
-    // block that may hold the maximum, go to the list for hi + lo scoring
-    constexpr float kEps = 1e-4f;
+  } else {
+    // In log2 units: keep when lE - d >= log2(alpha) + ehi, drop when
+    // lE + d < log2(alpha) + elo, each with a margin of 1e-4 relative plus
+    // what fp32 rounding of log energies of this size can add.  Decided
+    // blocks become +inf (kept) or 0 (dropped); the others, and every block
+    // that may hold the maximum, go to the list for hi + lo scoring
+    const float lal = alpha > 0.f ? __builtin_amdgcn_logf(alpha) : -INFINITY;
+    const float mrg = 1.4426e-4f + fmaxf(fabsf(ehi), fabsf(elo)) * 0x1p-20f;  // log2(1 + 1e-4) + rounding
     each_block([&](int J, float lb) {
-      const float e = SJ[J], d = dsc * lb;
-      const float up = e * __builtin_amdgcn_exp2f(d) * (1.f + kEps), dn = e * __builtin_amdgcn_exp2f(-d);
-      const bool keep = dn >= alpha * ehi * (1.f + kEps), drop = up < alpha * elo;
+      const float le = mJ[J], d = dsc * lb;
+      const float up = le + d + mrg, dn = le - d;
+      const bool keep = dn >= lal + ehi + mrg, drop = up < lal + elo;
       const bool maxc = up >= elo;
       const bool unc = !forced_block(J) && !keep && !drop;
       if (unc) atomicAdd(&nunc_sh, 1);
       if (unc || maxc) flg[atomicAdd(&nflag_sh, 1)] = J;
-      SJ[J] = keep ? INFINITY : (drop ? 0.f : e);
+      SJ[J] = keep ? INFINITY : 0.f;
     });
     __syncthreads();
     // nothing undecided: the bounds alone give the kept set
@@ -339,10 +423,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
       }
       __syncthreads();
     }
-    // hi + lo energies of the listed blocks; the maximum is among them.
+    // hi + lo energies E_J = S_J 2^(m_J - M) of the listed blocks, M the
+    // largest lE (any common reference serves); the maximum is among them.
     // Decided blocks hold +inf (kept) or 0 (dropped): with none re-scored the
     // threshold only has to separate those two
-    Emax = 0.f;
     thr = INFINITY;
     if (nflag > 0) {
       float le = 0.f;
@@ -352,8 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
         SJ[J] = e;
         le = fmaxf(le, e);
       }
-      Emax = block_max(le, red);
-      thr = alpha * Emax;
+      thr = alpha * block_max(le, red);
     }
   }
   int nsel = 0;
@@ -368,10 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DT == kF32 
       if (w0 + 1 < g.words) bits[s * g.words + w0 + 1] = (uint32_t)(m >> 32);
     }
     nsel += __popcll(m);
-    if (energies && in) energies[s * g.max_nj + J] = SJ[J] / Emax;
   }
-  if (energies)
-    for (int J = nc + threadIdx.x; J < g.max_nj; J += 256) energies[s * g.max_nj + J] = -1.f;
   if (lane == 0) nsel_w[wave] = nsel;
   __syncthreads();
   if (threadIdx.x == 0) {
