@@ -189,6 +189,7 @@ MeansLayout means_layout(const fp_problem* p, const HostGeo& hg) {
   m.vop = o; o = align256(o + rows * elem_size(p->dtype));
   m.klo8 = o; o = align256(o + (p->dtype == FP_E4M3 ? rows : 0));
   m.kbnd = o; o = align256(o + (size_t)hg.nb_pad * p->num_heads_kv * 4);
+  m.knrm = o; o = align256(o + (size_t)hg.nb_pad * p->num_heads_kv * 4);
   m.total = o;
   return m;
 }
@@ -234,6 +235,7 @@ WsLayout ws_layout(const fp_problem* p, const HostGeo& hg, const SplitPolicy& sp
   w.counts = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.scan_part = o; o = align256(o + (size_t)((hg.n_seg + 1023) / 1024 + 1) * 4);
   w.bits = o; o = align256(o + (with_select ? (size_t)hg.n_seg * hg.words * 4 : 0));
+  w.redo = o; o = align256(o + (with_select ? (size_t)hg.n_seg * 4 : 0));
   w.work = o; o = align256(o + (size_t)hg.n_seg * 4);
   w.wscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
   w.uscan = o; o = align256(o + (size_t)(hg.n_seg + 1) * 4);
@@ -377,7 +379,7 @@ fp_status fp_select(const fp_problem* prob, const fp_select_params* params, cons
   FP_LAUNCH(launch_meta(pr.g, st));
   FP_LAUNCH(launch_pool(pr.g, pr.ml, k, v, (char*)means, st));
   FP_LAUNCH(launch_score_select(pr.g, pr.ml, q, (const char*)means, params->alpha, params->sink_blocks,
-                                params->window_blocks, counts, bits, energies, st));
+                                params->window_blocks, counts, bits, energies, (int32_t*)(wsb + pr.wl.redo), st));
   FP_LAUNCH(launch_scan(counts, pr.hg.n_seg, cu, (int32_t*)(wsb + pr.wl.scan_part), st));
   FP_LAUNCH(launch_expand(pr.g, cu, bits, idx, idx_capacity, st));
   return FP_OK;

@@ -30,7 +30,8 @@ struct WsHeader {
   int32_t err;
   int32_t total_units;
   int32_t xcd_start[kXcds];    // first unit of each XCD's range (the next range's start ends it)
-  int32_t pad[32 - 2 - kXcds];
+  int32_t redo;                // segments the hi-only scoring left for full precision
+  int32_t pad[32 - 3 - kXcds];
   // units taken from each XCD's range, one 128-byte line apiece: atomics on
   // one line are serialised by the memory-side atomic unit
   int32_t xcd_counter[kXcds][32];
@@ -63,10 +64,12 @@ struct Geo {
 // Layout of the pooled-statistics buffer (byte offsets).
 struct MeansLayout {
   size_t kbar32, vbar32;  // float [nb_pad][hkv][128]
-  size_t khi, klo;        // bf16, MFMA B-operand order: [nb_pad/32][hkv][8][64][8]
+  size_t khi, klo;        // bf16 hi + lo of kbar * sl (sl: sigma log2 e, times c_q for E4M3),
+                          // MFMA B-operand order: [nb_pad/32][hkv][8][64][8]
   size_t kop, vop;        // element dtype, [nb_pad][hkv][128]: operands of correction steps
   size_t klo8;            // E4M3 only, [nb_pad][hkv][128]: kbar/c_k - kop, times 16, as E4M3
-  size_t kbnd;            // float [nb_pad][hkv]: |kbar lo|_2 over the dims (bounds the lo products)
+  size_t kbnd;            // float [nb_pad][hkv]: |lo|_2 over the dims (bounds the lo products)
+  size_t knrm;            // float [nb_pad][hkv]: |hi|_2 over the dims (scoring's per-block reference)
   size_t total;
 };
 
@@ -86,7 +89,7 @@ struct UnitRec {
 
 // Layout of the workspace (byte offsets).
 struct WsLayout {
-  size_t hdr, seg_off, blk_base, counts, scan_part, bits, work, wscan, uscan, units, part_o, part_ml, total;
+  size_t hdr, seg_off, blk_base, counts, scan_part, bits, redo, work, wscan, uscan, units, part_o, part_ml, total;
   int32_t umax;           // largest split count of one segment
 };
 
@@ -99,9 +102,9 @@ struct SplitPolicy {
 hipError_t launch_meta(const Geo& g, hipStream_t st);
 hipError_t launch_pool(const Geo& g, const MeansLayout& ml, const void* k, const void* v,
                        char* means, hipStream_t st);
-hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* q,
-                               const char* means, float alpha, int sink, int win,
-                               int32_t* counts, uint32_t* bits, float* energies, hipStream_t st);
+hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* q, const char* means,
+                               float alpha, int sink, int win, int32_t* counts, uint32_t* bits,
+                               float* energies, int32_t* redo, hipStream_t st);
 hipError_t launch_scan(const int32_t* counts, int64_t n, int32_t* cu, int32_t* part, hipStream_t st);
 hipError_t launch_expand(const Geo& g, const int32_t* cu, const uint32_t* bits, int32_t* idx,
                          int64_t cap, hipStream_t st);

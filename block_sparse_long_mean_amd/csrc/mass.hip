@@ -117,7 +117,8 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
   const float dk = DT == kE4M3 ? g.descale[1] : 1.f;
   const float l2e = 1.4426950408889634f;
   const float sl_k = g.scale * l2e * dq * dk;  // exact keys
-  const float sl_m = g.scale * l2e * dq;       // pooled means are stored descaled
+  // the pooled means' scoring operands are stored already multiplied by
+  // sigma log2 e (and c_q): their products are logits in log2 units
   const float inv_n = 1.f / (float)t.nrows;
 
   if (threadIdx.x == 0) err_sh = 0;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int R = rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          sum += __builtin_amdgcn_exp2f(fmaf(acc[r], sl_m, -lse2[R]));
+          sum += __builtin_amdgcn_exp2f(acc[r] - lse2[R]);
         }
       }
       sum += __shfl_xor(sum, 32, 64);

@@ -52,7 +52,10 @@ __global__ __launch_bounds__(1024) void meta_kernel(Geo g) {
     g.seg_off[g.nreq] = (int32_t)sseg[1023];
     g.blk_base[g.nreq] = (int32_t)sblk[1023];
   }
-  if (tid == 0) g.hdr->err = 0;
+  if (tid == 0) {
+    g.hdr->err = 0;
+    g.hdr->redo = 0;
+  }
 }
 
 // 8 consecutive elements of a K/V row as floats.
@@ -205,11 +208,18 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
       ((uint8_t*)(means + ml.klo8))[row_el] = (uint8_t)f32x2_to_e4m3x2(fminf(448.f, fmaxf(-448.f, r)), 0.f);
     }
   }
+  // The scoring operands: kbar times sl = sigma log2 e (E4M3: also c_q, the
+  // query scale), so that a query row's product with them is its logit in
+  // log2 units, split as hi + lo in bf16 and stored in MFMA B-operand order:
+  // [block/32][head][d/16][lane = block%32 + 32*((d%16)/8)][d%8]
+  const float sl = g.scale * 1.4426950408889634f * (DT == kE4M3 ? g.descale[0] : 1.f);
+  float hv = 0.f, lv = 0.f;
   if (which == 0) {
-    // kbar = hi + lo in bf16, stored in MFMA B-operand order:
-    // [block/32][head][d/16][lane = block%32 + 32*((d%16)/8)][d%8]
-    uint16_t hb = f32_to_bf16_bits(mean);
-    uint16_t lb = f32_to_bf16_bits(mean - bf16_bits_to_f32(hb));
+    const float ms = mean * sl;
+    const uint16_t hb = f32_to_bf16_bits(ms);
+    hv = bf16_bits_to_f32(hb);
+    const uint16_t lb = f32_to_bf16_bits(ms - hv);
+    lv = bf16_bits_to_f32(lb);
     int64_t jt = gb >> 5;
     int j = (int)(gb & 31);
     int ks = d >> 4, hh = (d >> 3) & 1, e = d & 7;
@@ -217,19 +227,20 @@ __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const 
     ((uint16_t*)(means + ml.khi))[o] = hb;
     ((uint16_t*)(means + ml.klo))[o] = lb;
   }
-  // |lo|_2 over the block's 128 dims (waves 0 and 1 hold K's dims): scoring
-  // with hi alone is off from hi + lo by at most |q|_2 times this
-  __shared__ float lsq[2];
-  float la = 0.f;
-  if (which == 0) {
-    const float hv = bf16_bits_to_f32(f32_to_bf16_bits(mean));
-    const float lv = bf16_bits_to_f32(f32_to_bf16_bits(mean - hv));
-    la = lv * lv;
+  // |lo|_2 and |hi|_2 over the block's 128 dims (waves 0 and 1 hold K's
+  // dims): scoring with hi alone is off from hi + lo by at most |q|_2 |lo|_2,
+  // and no logit of hi alone exceeds |q|_2 |hi|_2 (Cauchy-Schwarz)
+  __shared__ float lsq[2], hsq[2];
+  const float la = wave_sum(lv * lv), ha = wave_sum(hv * hv);
+  if ((tid & 63) == 0 && tid < 128) {
+    lsq[tid >> 6] = la;
+    hsq[tid >> 6] = ha;
   }
-  la = wave_sum(la);
-  if ((tid & 63) == 0 && tid < 128) lsq[tid >> 6] = la;
   __syncthreads();
-  if (tid == 0) ((float*)(means + ml.kbnd))[gb * g.hkv + h] = sqrtf(lsq[0] + lsq[1]);
+  if (tid == 0) {
+    ((float*)(means + ml.kbnd))[gb * g.hkv + h] = sqrtf(lsq[0] + lsq[1]);
+    ((float*)(means + ml.knrm))[gb * g.hkv + h] = sqrtf(hsq[0] + hsq[1]);
+  }
 }
 
 hipError_t launch_meta(const Geo& g, hipStream_t st) {
