@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     Geo g, WsLayout wl, char* __restrict__ ws, MeansLayout ml, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ idx, const char* __restrict__ means, int correction,
-    void* __restrict__ out, float* __restrict__ lse) {
+    void* __restrict__ out, float* __restrict__ lse, int nwg) {
   using C = Cfg<DT>;
   using Op = typename Tr<DT>::Op;
   constexpr int KPL = C::KPL;
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 
   // the wave index is uniform: in a scalar register, addresses derived from it
   // (LDS DMA destinations) need no per-instruction readfirstlane
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = thread_x(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // this wave's LDS base of the DMA destinations: the bf16 tiles' 1 KB pieces
   // wave + 4 i, the e4m3 tiles' rows 16 wave + ...; then a stage offset and an
   // immediate per DMA (held opaque, like sb)
@@ -412,8 +412,8 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   // once it is exhausted, from the other ranges.  The atomic for the next unit
   // is issued when a unit starts and its result is first needed when the
   // unit ends, so its latency hides behind the unit's loads.
-  const int nx = gridDim.x % kXcds == 0 ? kXcds : 1;
-  const int xcd = blockIdx.x % nx;
+  const int nx = nwg % kXcds == 0 ? kXcds : 1;  // nwg: the grid's workgroup count
+  const int xcd = block_x() % nx;
   auto range_of = [&](int x, int& lo, int& hi) {
     lo = nx == kXcds ? g.hdr->xcd_start[x] : 0;
     hi = nx == kXcds && x + 1 < kXcds ? g.hdr->xcd_start[x + 1] : g.hdr->total_units;
@@ -433,6 +433,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
   int own_lo, own_hi;
   range_of(xcd, own_lo, own_hi);
   __shared__ int sh_unit;
+  __shared__ int bad_w[4];  // per wave: some lane of the unit saw malformed input
   if (tid == 0) {
     const int kk = atomicAdd(&g.hdr->xcd_counter[xcd][0], 1);
     sh_unit = kk < own_hi - own_lo ? own_hi - 1 - kk : steal(xcd + 1);
@@ -1836,7 +1837,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
     // NaN bit patterns instead (a separate branch, so no float select is involved)
     if (err) atomicOr(&g.hdr->err, (int)err);
     if (tid == 0) sh_unit = ticket < own_hi - own_lo ? own_hi - 1 - ticket : steal(xcd + 1);
-    const bool bad = __syncthreads_or(err != 0) != 0;
+    // each wave rewrites its own flag every unit, and a wave reaches this
+    // write only after every wave has passed the unit's first barrier, that
+    // is after every read of the previous unit's flags
+    if (lane == 0) bad_w[wave] = __ballot(err != 0) != 0;
+    __syncthreads();
+    const bool bad = (bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
     const float2 lp = with_other_half(l_i);
     const float l_tot = lp.x + lp.y;
     if (DT == kBF16 && un.nsplit == 1 && !bad) {
@@ -1944,13 +1950,13 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 template <int DT>
 __global__ __launch_bounds__(256) void combine_kernel(Geo g, WsLayout wl, const char* __restrict__ ws,
                                                       void* __restrict__ out, float* __restrict__ lse) {
-  const int64_t s = blockIdx.x;
+  const int64_t s = block_x();
   const int32_t* nsplit = (const int32_t*)(ws + wl.counts);
   const int U = nsplit[s];
   if (U <= 1) return;
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
-  const int r = threadIdx.x >> 1, n0 = (threadIdx.x & 1) * 64;
+  const int r = thread_x() >> 1, n0 = (thread_x() & 1) * 64;
   if (r >= t.nrows) return;
   const float* po = (const float*)(ws + wl.part_o);
   const float* pml = (const float*)(ws + wl.part_ml);
@@ -2003,7 +2009,7 @@ static hipError_t launch_attn_t(const Geo& g, const WsLayout& wl, char* ws, cons
   hipError_t e = set_lds_limit((const void*)attn_kernel<DT, DENSE, AM, VC>, Cfg<DT>::LDS);
   if (e != hipSuccess) return e;
   attn_kernel<DT, DENSE, AM, VC><<<grid, 256, Cfg<DT>::LDS, st>>>(g, wl, ws, ml, q, k, v, cu, idx, means,
-                                                                      correction, out, lse);
+                                                                      correction, out, lse, grid);
   return hipGetLastError();
 }
 

@@ -10,6 +10,15 @@
 
 namespace fp {
 
+// Work-item and work-group ids read straight from the hardware registers.
+// HIP's threadIdx / blockIdx / gridDim and __syncthreads_or go through
+// device-library functions that are not inlined into code built with IEEE
+// mode off (their function attributes differ), and each such call costs a
+// full register save around it; these builtins need none.
+__device__ __forceinline__ int thread_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int block_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int block_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -69,7 +78,7 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 
 // Inclusive prefix sum over the lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
+  const int lane = thread_x() & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     int y = __shfl_up(x, o, 64);

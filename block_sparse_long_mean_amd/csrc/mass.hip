@@ -107,10 +107,10 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
   int* qpos = (int*)(lse2 + kRows);                           // row's query index (position - off)
   __shared__ int err_sh;
 
-  const int64_t s = blockIdx.x;
+  const int64_t s = block_x();
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = thread_x() & 63, wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int nc = t.beta1 + 1;
   const float dq = DT == kE4M3 ? g.descale[0] : 1.f;
@@ -121,9 +121,9 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
   // sigma log2 e (and c_q): their products are logits in log2 units
   const float inv_n = 1.f / (float)t.nrows;
 
-  if (threadIdx.x == 0) err_sh = 0;
-  if (threadIdx.x < kRows) {
-    const int r = threadIdx.x;
+  if (thread_x() == 0) err_sh = 0;
+  if (thread_x() < kRows) {
+    const int r = thread_x();
     float l = INFINITY;  // padding rows: exp2(x - inf) = 0
     int qi = 0;
     if (r < t.nrows) {
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
     const float tot = wave_sum(acc_sum);
     if (lane == 0) mass[s * g.max_nj + J] = tot * inv_n;
   }
-  for (int J = nc + threadIdx.x; J < g.max_nj; J += 256) mass[s * g.max_nj + J] = -1.f;
+  for (int J = nc + thread_x(); J < g.max_nj; J += 256) mass[s * g.max_nj + J] = -1.f;
 
   if (sur) {
     // surrogate: 32-block column tiles of the pooled means, blocks J < beta
@@ -203,10 +203,10 @@ __global__ __launch_bounds__(256) void block_mass_kernel(Geo g, MeansLayout ml, 
       const int J = jt * 32 + col;
       if (half == 0 && J < t.beta) sur[s * g.max_nj + J] = (float)kBlock * sum * inv_n;
     }
-    for (int J = t.beta + threadIdx.x; J < g.max_nj; J += 256) sur[s * g.max_nj + J] = J < nc ? 0.f : -1.f;
+    for (int J = t.beta + thread_x(); J < g.max_nj; J += 256) sur[s * g.max_nj + J] = J < nc ? 0.f : -1.f;
   }
   __syncthreads();
-  if (threadIdx.x == 0 && err_sh) atomicOr(&g.hdr->err, err_sh);
+  if (thread_x() == 0 && err_sh) atomicOr(&g.hdr->err, err_sh);
 }
 
 hipError_t launch_block_mass(const Geo& g, const MeansLayout& ml, const void* q, const void* k,

@@ -16,7 +16,7 @@ namespace fp {
 __global__ __launch_bounds__(1024) void meta_kernel(Geo g) {
   __shared__ int64_t sseg[1024];
   __shared__ int64_t sblk[1024];
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int per = (g.nreq + 1023) / 1024;
   const int lo = tid * per;
   const int hi = min(lo + per, g.nreq);
@@ -90,9 +90,9 @@ template <int DT>
 __global__ __launch_bounds__(256) void pool_kernel(Geo g, MeansLayout ml, const void* __restrict__ k,
                                                    const void* __restrict__ v, char* __restrict__ means) {
   __shared__ float red[2][16][kD];
-  const int64_t gb = blockIdx.x;
-  const int h = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int64_t gb = block_x();
+  const int h = block_y();
+  const int tid = thread_x();
   // request owning padded block gb
   int lo = 0, hi = g.nreq - 1;
   while (lo < hi) {

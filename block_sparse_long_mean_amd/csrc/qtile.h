@@ -10,9 +10,9 @@ constexpr int kQPitch = kD + 8;  // bf16 elements per staged Q row (bank spread)
 
 __device__ __forceinline__ float block_max(float x, float* red) {
   x = wave_max(x);
-  const int w = threadIdx.x >> 6;
+  const int w = thread_x() >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = x;
+  if ((thread_x() & 63) == 0) red[w] = x;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
@@ -21,7 +21,7 @@ __device__ __forceinline__ float block_max(float x, float* red) {
 template <int DT>
 __device__ __forceinline__ void stage_q(const Geo& g, const SegCoord& c, const TileGeo& t,
                                         const void* q, uint16_t* qh, uint16_t* ql) {
-  const int tid = threadIdx.x;
+  const int tid = thread_x();
   const int64_t r0 = c.I * kRows;
   // all of a thread's loads are issued before the first is used
   if constexpr (DT == kBF16) {

@@ -39,7 +39,7 @@ __device__ __forceinline__ void seg_work(const Geo& g, const int32_t* cu, int64_
 __global__ __launch_bounds__(256) void sched_count_kernel(Geo g, const int32_t* __restrict__ cu, int dense,
                                                           int correction, SplitPolicy sp, int32_t* work,
                                                           int32_t* nsplit) {
-  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = (int64_t)block_x() * 256 + thread_x();
   if (s >= g.n_seg) return;
   int U, W;
   seg_work(g, cu, s, dense, correction, sp, U, W);
@@ -52,10 +52,10 @@ __global__ __launch_bounds__(256) void sched_place_kernel(Geo g, const int32_t* 
                                                           const int32_t* __restrict__ uscan,
                                                           const int32_t* __restrict__ nsplit,
                                                           const int32_t* __restrict__ cu, UnitRec* units) {
-  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = (int64_t)block_x() * 256 + thread_x();
   const int64_t n = g.n_seg;
   const int64_t wtot = max(1, wscan[n]);
-  if (blockIdx.x == 0 && threadIdx.x < kXcds) g.hdr->xcd_counter[threadIdx.x][0] = 0;
+  if (block_x() == 0 && thread_x() < kXcds) g.hdr->xcd_counter[thread_x()][0] = 0;
   if (s == 0) g.hdr->total_units = uscan[n];
   if (s >= n) return;
   const int x = (int)min<int64_t>(kXcds - 1, (int64_t)wscan[s] * kXcds / wtot);

@@ -33,7 +33,7 @@ namespace fp {
 __device__ __forceinline__ float other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   // lanes 0-31 get lane + 32's x in r[1]; lanes 32-63 get lane - 32's in r[0]
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  return __uint_as_float((thread_x() & 32) ? r[0] : r[1]);
 }
 
 // What both scoring kernels need of one segment.
@@ -69,14 +69,14 @@ __device__ __forceinline__ ScoreSeg score_seg(const Geo& g, const MeansLayout& m
 
 // A operand of the staged tile: rows rt*32 + col, dims 16 ks + 8 half .. + 7
 __device__ __forceinline__ bf16x8 q_op(const uint16_t* qs, int rt, int ks) {
-  const int lane = threadIdx.x & 63;
+  const int lane = thread_x() & 63;
   return *(const bf16x8*)(qs + (rt * 32 + (lane & 31)) * kQPitch + 8 * (lane >> 5) + ks * 16);
 }
 
 // Padding rows of a ragged tile: the lane's register r of row tile rt holds
 // row rt*32 + 8*(r/4) + 4*half + r%4.
 __device__ __forceinline__ void mask_rows(f32x16& v, int rt, int nrows) {
-  const int half = (threadIdx.x >> 5) & 1;
+  const int half = (thread_x() >> 5) & 1;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     if (rt * 32 + 8 * (r >> 2) + 4 * half + (r & 3) >= nrows) v[r] = -INFINITY;
@@ -89,7 +89,7 @@ __device__ __forceinline__ void mask_rows(f32x16& v, int rt, int nrows) {
 __device__ __forceinline__ void write_selection(const Geo& g, const ScoreSeg& z, const float* SJ, float thr,
                                                 int sink, int win, int32_t* counts, uint32_t* bits,
                                                 int* nsel_w) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = thread_x() & 63, wave = thread_x() >> 6;
   const TileGeo& t = z.t;
   int nsel = 0;
   for (int base = wave * 64; base < z.nc; base += 256) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void write_selection(const Geo& g, const ScoreSeg& z,
   }
   if (lane == 0) nsel_w[wave] = nsel;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (thread_x() == 0) {
     const int tot = nsel_w[0] + nsel_w[1] + nsel_w[2] + nsel_w[3];
     const int trim = (int64_t)kTile * (2 * t.beta1 + 1) > t.t1 ? 1 : 0;
     counts[z.s] = 2 * tot - trim;
@@ -138,9 +138,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   __shared__ int nsel_w[4], nflag_sh, nunc_sh;
 
   SegCoord c;
-  const ScoreSeg z = score_seg(g, ml, means, blockIdx.x, c);
+  const ScoreSeg z = score_seg(g, ml, means, block_x(), c);
   const TileGeo& t = z.t;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = thread_x() & 63, wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int nc = z.nc, njt = z.njt, nrows = t.nrows;
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   float kb4[4] = {0.f, 0.f, 0.f, 0.f};  // |lo_J|_2 of this thread's first four blocks
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int J = threadIdx.x + 256 * k;
+    const int J = thread_x() + 256 * k;
     if (J < nc) kb4[k] = z.kbnd[(int64_t)J * g.hkv];
   }
   stage_q<DT>(g, c, t, q, qh, nullptr);
@@ -242,10 +242,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   auto each_block = [&](auto&& body) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int J = threadIdx.x + 256 * k;
+      const int J = thread_x() + 256 * k;
       if (J < nc) body(J, kb4[k]);
     }
-    for (int J = threadIdx.x + 1024; J < nc; J += 256) body(J, z.kbnd[(int64_t)J * g.hkv]);
+    for (int J = thread_x() + 1024; J < nc; J += 256) body(J, z.kbnd[(int64_t)J * g.hkv]);
   };
   float lhi = -INFINITY, llo = -INFINITY, lmx = -INFINITY;
   bool bad = false;
@@ -266,10 +266,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     pm[2][wave] = lmx;
     nsel_w[wave] = wbad;
   }
-  if (threadIdx.x == 0) nflag_sh = nunc_sh = 0;
+  if (thread_x() == 0) nflag_sh = nunc_sh = 0;
   __syncthreads();
   if ((nsel_w[0] | nsel_w[1] | nsel_w[2] | nsel_w[3]) != 0) {
-    if (threadIdx.x == 0) redo[atomicAdd(&g.hdr->redo, 1)] = (int32_t)z.s;
+    if (thread_x() == 0) redo[atomicAdd(&g.hdr->redo, 1)] = (int32_t)z.s;
     return;  // the whole workgroup: the flags are in LDS
   }
   const float ehi = fmaxf(fmaxf(pm[0][0], pm[0][1]), fmaxf(pm[0][2], pm[0][3]));
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   float thr = INFINITY;
   if (nflag > 0) {
     float le = 0.f;
-    for (int i = threadIdx.x; i < nflag; i += 256) le = fmaxf(le, SJ[flg[i]]);
+    for (int i = thread_x(); i < nflag; i += 256) le = fmaxf(le, SJ[flg[i]]);
     thr = alpha * block_max(le, red);
   }
   write_selection(g, z, SJ, thr, sink, win, counts, bits, nsel_w);
@@ -368,7 +368,7 @@ template <int DT, bool LIST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void score_exact_kernel(
     Geo g, MeansLayout ml, const void* __restrict__ q, const char* __restrict__ means, float alpha, int sink,
     int win, int32_t* __restrict__ counts, uint32_t* __restrict__ bits, float* __restrict__ energies,
-    const int32_t* __restrict__ redo) {
+    const int32_t* __restrict__ redo, int nwg) {
   extern __shared__ __align__(16) char smem[];
   constexpr int NQ = DT == kF32 ? 2 : 1;
   uint16_t* qh = (uint16_t*)smem;
@@ -377,11 +377,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   float* SJ = mJ + g.max_nj;
   __shared__ float red[4];
   __shared__ int nsel_w[4];
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = thread_x() & 63, wave = __builtin_amdgcn_readfirstlane(thread_x() >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int64_t nwork = LIST ? (int64_t)g.hdr->redo : g.n_seg;
 
-  for (int64_t i = blockIdx.x; i < nwork; i += gridDim.x) {
+  for (int64_t i = block_x(); i < nwork; i += nwg) {  // nwg: the grid's workgroup count
     const int64_t s = LIST ? (int64_t)redo[i] : i;
     SegCoord c;
     const ScoreSeg z = score_seg(g, ml, means, s, c);
@@ -483,18 +483,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     __syncthreads();
     // E_J = S_J 2^(m_J - M), M = max_J m_J; then keep E_J >= alpha max E or forced
     float lm = -INFINITY;
-    for (int J = threadIdx.x; J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
+    for (int J = thread_x(); J < nc; J += 256) lm = fmaxf(lm, mJ[J]);
     const float M = block_max(lm, red);
     float le = 0.f;
-    for (int J = threadIdx.x; J < nc; J += 256) {
+    for (int J = thread_x(); J < nc; J += 256) {
       const float e = SJ[J] * __builtin_amdgcn_exp2f(mJ[J] - M);
       SJ[J] = e;
       le = fmaxf(le, e);
     }
     const float Emax = block_max(le, red);  // >= 1: the block attaining M has S >= 1
     if (energies) {
-      for (int J = threadIdx.x; J < nc; J += 256) energies[s * g.max_nj + J] = SJ[J] / Emax;
-      for (int J = nc + threadIdx.x; J < g.max_nj; J += 256) energies[s * g.max_nj + J] = -1.f;
+      for (int J = thread_x(); J < nc; J += 256) energies[s * g.max_nj + J] = SJ[J] / Emax;
+      for (int J = nc + thread_x(); J < g.max_nj; J += 256) energies[s * g.max_nj + J] = -1.f;
     }
     write_selection(g, z, SJ, alpha * Emax, sink, win, counts, bits, nsel_w);
     __syncthreads();  // LDS is reused by the next segment
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // passes: 1024-entry blocks reduce to partial sums (scan_part_kernel), then
 // every block rescans its entries on top of the sum of the partials before it.
 __device__ __forceinline__ int block_excl_scan_1024(int x, int* sh, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = thread_x() & 63, w = thread_x() >> 6;
   const int incl = wave_incl_scan(x);
   if (lane == 63) sh[w] = incl;
   __syncthreads();
@@ -525,10 +525,10 @@ __device__ __forceinline__ int block_excl_scan_1024(int x, int* sh, int& total) 
 __global__ __launch_bounds__(1024) void scan_part_kernel(const int32_t* __restrict__ counts, int64_t n,
                                                          int32_t* __restrict__ part) {
   __shared__ int sh[40];
-  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const int64_t i = (int64_t)block_x() * 1024 + thread_x();
   int total;
   block_excl_scan_1024(i < n ? counts[i] : 0, sh, total);
-  if (threadIdx.x == 0) part[blockIdx.x] = total;
+  if (thread_x() == 0) part[block_x()] = total;
 }
 
 __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restrict__ counts, int64_t n,
@@ -536,14 +536,14 @@ __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restr
   __shared__ int sh[40];
   __shared__ int base_sh;
   // offset of this block: sum of the partials before it (one wave)
-  if (threadIdx.x < 64) {
+  if (thread_x() < 64) {
     int acc = 0;
-    for (int b = threadIdx.x; b < (int)blockIdx.x; b += 64) acc += part[b];
+    for (int b = thread_x(); b < (int)block_x(); b += 64) acc += part[b];
     acc = wave_sum_i(acc);
-    if (threadIdx.x == 0) base_sh = acc;
+    if (thread_x() == 0) base_sh = acc;
   }
   __syncthreads();
-  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const int64_t i = (int64_t)block_x() * 1024 + thread_x();
   const int x = i < n ? counts[i] : 0;
   int total;
   const int ex = block_excl_scan_1024(x, sh, total);
@@ -556,9 +556,9 @@ __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restr
 __global__ __launch_bounds__(256) void expand_kernel(Geo g, const int32_t* __restrict__ cu,
                                                      const uint32_t* __restrict__ bits,
                                                      int32_t* __restrict__ idx, int64_t cap) {
-  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t s = (int64_t)block_x() * 4 + (thread_x() >> 6);
   if (s >= g.n_seg) return;
-  const int lane = threadIdx.x & 63;
+  const int lane = thread_x() & 63;
   const SegCoord c = seg_coord(g, s);
   const TileGeo t = tile_geo(g, c);
   const int64_t start = cu[s];
@@ -597,11 +597,11 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
     if (g.dtype == kBF16) {
       score_hi_kernel<kBF16><<<grid, 256, la, st>>>(g, ml, q, means, alpha, sink, win, counts, bits, redo);
       score_exact_kernel<kBF16, true><<<gl, 256, lb, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
-                                                            nullptr, redo);
+                                                            nullptr, redo, (int)gl.x);
     } else {
       score_hi_kernel<kE4M3><<<grid, 256, la, st>>>(g, ml, q, means, alpha, sink, win, counts, bits, redo);
       score_exact_kernel<kE4M3, true><<<gl, 256, lb, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
-                                                            nullptr, redo);
+                                                            nullptr, redo, (int)gl.x);
     }
     return hipGetLastError();
   }
@@ -615,15 +615,15 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
   switch (g.dtype) {
     case kBF16:
       score_exact_kernel<kBF16, false><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
-                                                               energies, nullptr);
+                                                               energies, nullptr, (int)grid.x);
       break;
     case kF32:
       score_exact_kernel<kF32, false><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
-                                                              energies, nullptr);
+                                                              energies, nullptr, (int)grid.x);
       break;
     default:
       score_exact_kernel<kE4M3, false><<<grid, 256, lds, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
-                                                               energies, nullptr);
+                                                               energies, nullptr, (int)grid.x);
       break;
   }
   return hipGetLastError();
