@@ -120,10 +120,13 @@ __device__ __forceinline__ void write_selection(const Geo& g, const ScoreSeg& z,
 // matrix of the staged rows) is an upper bound of every hi-only logit of block
 // J (Cauchy-Schwarz).  It enters as the MFMA's initial accumulator, so the
 // products come out as x_rJ - c_J and each weight costs one exp and one add.
-// With every weight <= 1 (up to rounding) no sum overflows; a block whose
-// largest logit lies more than 90 below c_J (sum < 2^-90, where terms that
-// flush to zero could matter), or an infinite or NaN sum, sends the segment to
-// the list for full-precision scoring.
+// With every weight <= 1 (up to rounding) no sum overflows.  Weights below
+// 2^-126 may flush to zero: at most 127 of them lose less than 2^-119, which
+// against a sum >= 2^-100 is below 2^-19 of it (far inside the decisions'
+// margin).  A sum below 2^-100 sends the column tile through again with a
+// lower reference; a block whose logits all lie more than 400 below its
+// bound, or an infinite or NaN sum, sends the segment to the list for
+// full-precision scoring.
 template <int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void score_hi_kernel(
     Geo g, MeansLayout ml, const void* __restrict__ q, const char* __restrict__ means, float alpha, int sink,
@@ -191,37 +194,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   // ahead.  Leaves lE_J = c_J + log2 S_J (or +inf) in lE.
   auto tile_hi = [&](auto ragged_tag, int J, const bf16x8 (&b)[8], float cref) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
-    f32x16 cinit;
+    // A sum below 2^-100 means every logit of the block lies more than 100
+    // below the reference; the column tile is then computed again with that
+    // block's reference lowered by 100 (no weight can exceed 1 against it),
+    // up to three times (logits down to 400 below the bound).  The lane halves
+    // holding one block see the same merged sum and lower their reference
+    // together.
+    for (int pass = 0;; ++pass) {
+      f32x16 cinit;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[r] = -cref;
-    float s0 = 0.f, s1 = 0.f;
-    auto weights = [&](int rt, f32x16& v, int k) __attribute__((always_inline)) {
-      if (RAGGED && k == 0) mask_rows(v, rt, nrows);
-      s0 += __builtin_amdgcn_exp2f(v[2 * k]);
-      s1 += __builtin_amdgcn_exp2f(v[2 * k + 1]);
-    };
-    f32x16 acc[2];
-    bf16x8 ring[2];
-    ring[0] = q_op(qh, 0, 0);
-    ring[1] = q_op(qh, 0, 1);
+      for (int r = 0; r < 16; ++r) cinit[r] = -cref;
+      float s0 = 0.f, s1 = 0.f;
+      auto weights = [&](int rt, f32x16& v, int k) __attribute__((always_inline)) {
+        if (RAGGED && k == 0) mask_rows(v, rt, nrows);
+        s0 += __builtin_amdgcn_exp2f(v[2 * k]);
+        s1 += __builtin_amdgcn_exp2f(v[2 * k + 1]);
+      };
+      f32x16 acc[2];
+      bf16x8 ring[2];
+      ring[0] = q_op(qh, 0, 0);
+      ring[1] = q_op(qh, 0, 1);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
+      for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = ring[ks & 1];
-        const int nrt = ks + 2 < 8 ? rt : rt + 1, nks = (ks + 2) & 7;
-        if (nrt < 4) ring[ks & 1] = q_op(qh, nrt, nks);
-        acc[rt & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[ks], ks == 0 ? cinit : acc[rt & 1], 0, 0, 0);
-        if (rt > 0) weights(rt - 1, acc[(rt - 1) & 1], ks);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 a = ring[ks & 1];
+          const int nrt = ks + 2 < 8 ? rt : rt + 1, nks = (ks + 2) & 7;
+          if (nrt < 4) ring[ks & 1] = q_op(qh, nrt, nks);
+          acc[rt & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[ks], ks == 0 ? cinit : acc[rt & 1], 0, 0, 0);
+          if (rt > 0) weights(rt - 1, acc[(rt - 1) & 1], ks);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) weights(3, acc[1], k);
-    const float sm = s0 + s1;
-    const float tot = sm + other_half(sm);  // the other lane half holds the block's other 64 rows
-    if (half == 0 && J < nc)
-      lE[J] = tot >= 0x1p-90f && tot < INFINITY ? cref + __builtin_amdgcn_logf(tot) : INFINITY;
+      for (int k = 0; k < 8; ++k) weights(3, acc[1], k);
+      const float sm = s0 + s1;
+      const float tot = sm + other_half(sm);  // the other lane half holds the block's other 64 rows
+      const bool low = !(tot >= 0x1p-100f);   // also NaN
+      if (pass < 3 && __ballot(low && J < nc) != 0) {
+        if (low) cref -= 100.f;
+        continue;
+      }
+      if (half == 0 && J < nc) lE[J] = !low && tot < INFINITY ? cref + __builtin_amdgcn_logf(tot) : INFINITY;
+      break;
+    }
   };
   auto sweep = [&](auto ragged_tag) {
     for (int jt = wave; jt < njt; jt += 4) {
@@ -593,7 +609,7 @@ hipError_t launch_score_select(const Geo& g, const MeansLayout& ml, const void* 
     if (e == hipSuccess) e = set_lds_limit(fb, q1 + (size_t)kMaxBlocks * 8);
     if (e != hipSuccess) return e;
     const size_t la = q1 + (size_t)g.max_nj * 12, lb = q1 + (size_t)g.max_nj * 8;
-    const dim3 gl((unsigned)std::min<int64_t>(g.n_seg, 1024));
+    const dim3 gl((unsigned)std::min<int64_t>(g.n_seg, 256));  // the list is usually empty
     if (g.dtype == kBF16) {
       score_hi_kernel<kBF16><<<grid, 256, la, st>>>(g, ml, q, means, alpha, sink, win, counts, bits, redo);
       score_exact_kernel<kBF16, true><<<gl, 256, lb, st>>>(g, ml, q, means, alpha, sink, win, counts, bits,
