@@ -1424,7 +1424,11 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
         // one iteration, reading stage PAR and filling the other; P holds the
         // previous step's probabilities until the five MFMAs that read them have
         // issued, then the current step's
-        auto iter = [&]() __attribute__((always_inline)) {
+        // KIND: the step whose softmax the iteration takes (0 a listed tile that
+        // reaches past the first row's position, 1 another listed tile, 2 a
+        // correction chunk); the steps come in that order, one loop per kind
+        auto iter = [&](auto kind_tag) __attribute__((always_inline)) {
+          constexpr int KIND = decltype(kind_tag)::value;
           const int PAR = par;
           const int WR = 1 - PAR;  // stage the DMA fills
           // the step after next, and this iteration's DMA: K(s_{k+2}) and V(s_k)
@@ -1436,12 +1440,12 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
             pen3(ts2, nxt2);
           }
           dma_v(WR, cur, cur_tile);
-          const bool chunk = cur >= T;
+          constexpr bool chunk = KIND == 2;
           // logits in log2 units are S * slk: a tile step holds raw dot products,
           // a correction step gets its scale and offset (+7, or -inf where masked)
           // applied here; keys past a row's position are masked here
           const float slk = chunk ? 1.f : sl;
-          if (chunk) {
+          if constexpr (chunk) {
             const f32x4* penp = (const f32x4*)(smem + PEN3 + ts * 256) + half * 8;
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
@@ -1451,7 +1455,7 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) S[jt][4 * r4 + e] = fmaf(S[jt][4 * r4 + e], sl, pv[e]);
               }
-          } else if (cur_tile * kTile + kTile - 1 > t.t0) {
+          } else if constexpr (KIND == 0) {
             const int lim = pos - cur_tile * kTile - 4 * half;  // key j visible iff j <= pos - 64 p
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt)
@@ -1560,10 +1564,20 @@ __global__ __launch_bounds__(256, Cfg<DT>::WGS) void attn_kernel(
           nxt = nxt2;
           nxt_tile = nxt2_tile;
         };
-        // steps in order (listed tiles, then correction chunks)
-        while (cur < it1) {
-          iter();
+        // steps in order (listed tiles, the masked ones first, then correction chunks)
+        while (cur < it1 && cur < T && cur_tile * kTile + kTile - 1 > t.t0) {
+          iter(std::integral_constant<int, 0>{});
           par ^= 1;
+        }
+        while (cur < it1 && cur < T) {
+          iter(std::integral_constant<int, 1>{});
+          par ^= 1;
+        }
+        if constexpr (!DENSE) {
+          while (cur < it1) {
+            iter(std::integral_constant<int, 2>{});
+            par ^= 1;
+          }
         }
         // PV of the last step: its V tile sits in the stage the last iteration
         // filled, which par now names
