@@ -45,8 +45,8 @@ def test_bounded_scoring_keeps_the_exact_set(name, alpha, sink, win):
 
 def test_bounded_scoring_extremes():
     """Ragged and single-row tiles, alpha 0 (everything kept) and alpha 1 (only
-    blocks tied with the maximum).  Tiles with at most 64 candidate blocks are
-    always scored with hi + lo; the 20000-token request has longer ones."""
+    blocks tied with the maximum), on tiles from one candidate block (the
+    1-token request) to 157 (the 20000-token request)."""
     b = synth.make_batch([1, 130, 2500, 7000, 20000], 32, 4, 128, seed=53, dtype="bf16", clusters=True,
                          diag_bias=True)
     for alpha in (0.0, 1.0, 0.5):
