@@ -226,11 +226,17 @@ def test_bad_idx_is_flagged():
     assert run.device_error() & 2
 
 
-@pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "bf16"), (16, 8, "bf16"), (32, 2, "bf16"), (8, 8, "e4m3")])
+@pytest.mark.parametrize(
+    "hq,hkv,dtype",
+    [(8, 8, "bf16"), (16, 8, "bf16"), (32, 2, "bf16"), (8, 8, "e4m3"), (64, 1, "bf16"), (128, 1, "bf16"),
+     (128, 1, "e4m3")])
 def test_group_sizes(hq, hkv, dtype):
     """GQA group sizes other than 8: g = 1 (a 128-row tile spans two key tiles,
     so rows of the first half see nothing in the second; masked steps with fully
-    masked rows), g = 2 and g = 16; full CSR and sampled attention."""
+    masked rows), g = 2, g = 16, g = 64 (two positions per tile) and the largest,
+    g = 128 (one position per tile: every tile is one query position's heads, so
+    a request has as many segments per KV head as tokens); full CSR and sampled
+    attention."""
     _print_case("group", hq=hq, hkv=hkv, dtype=dtype)
     b = synth.make_batch([1000, 2500, 333], hq, hkv, 128, seed=37, dtype="bf16", clusters=True, diag_bias=True)
     if dtype == "e4m3":
