@@ -16,7 +16,7 @@
  *
  * Everything is computed in double precision, one row / one block at a time,
  * in the order the pages state it.  Readings taken where the pages leave a
- * step open are marked READING and listed in the design notes.
+ * step open are marked READING where they are applied.
  *
  * Conventions shared with every caller (they are definitions of the problem,
  * not of the GPU path):
