@@ -569,6 +569,9 @@ __global__ __launch_bounds__(1024) void scan_final_kernel(const int32_t* __restr
 
 // One wave per segment: ballot + prefix count turn the selection bits into the
 // ascending list of physical tile ids (logical block J -> tiles 2J, 2J+1).
+// The segment's bit words are loaded once, one per lane (64 words = 2048
+// blocks per load), and handed to the lanes of each 64-block step by a
+// cross-lane permute, so that the steps do not wait on memory one by one.
 __global__ __launch_bounds__(256) void expand_kernel(Geo g, const int32_t* __restrict__ cu,
                                                      const uint32_t* __restrict__ bits,
                                                      int32_t* __restrict__ idx, int64_t cap) {
@@ -579,11 +582,16 @@ __global__ __launch_bounds__(256) void expand_kernel(Geo g, const int32_t* __res
   const TileGeo t = tile_geo(g, c);
   const int64_t start = cu[s];
   const int nc = t.beta1 + 1;  // blocks holding a key visible to some row
+  const int nw = (nc + 31) >> 5;
   int o = 0;
+  uint32_t wd = 0;
   for (int base = 0; base < nc; base += 64) {
+    const int w0 = base >> 5;  // first word of this step
+    if ((w0 & 63) == 0) wd = w0 + lane < nw ? bits[s * g.words + w0 + lane] : 0u;
     const int J = base + lane;
-    bool sel = false;
-    if (J < nc) sel = (bits[s * g.words + (J >> 5)] >> (J & 31)) & 1u;
+    // word (J >> 5) sits in lane (J >> 5) & 63 of this word group
+    const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(((w0 & 63) + (lane >> 5)) << 2, (int)wd);
+    const bool sel = J < nc && ((w >> (J & 31)) & 1u);
     const uint64_t m = __ballot(sel);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
     if (sel) {
