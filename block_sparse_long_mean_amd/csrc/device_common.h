@@ -110,11 +110,13 @@ __device__ __forceinline__ SegCoord seg_coord(const Geo& g, int64_t s) {
   }
   SegCoord c;
   c.b = lo;
-  int64_t local = s - g.seg_off[lo];
-  int64_t nt = ((int64_t)g.seg_off[lo + 1] - g.seg_off[lo]) / g.hkv;
+  // 32-bit division: segment counts stay below 2^31 / 16 (checked on the
+  // host), and a 64-bit division expands to ~140 scalar instructions
+  const int local = (int)(s - g.seg_off[lo]);
+  int nt = (g.seg_off[lo + 1] - g.seg_off[lo]) / g.hkv;
   if (nt < 1) nt = 1;
-  c.h = (int)(local / nt);
-  c.I = local - (int64_t)c.h * nt;
+  c.h = local / nt;
+  c.I = local - c.h * nt;
   c.row0 = g.cu_q[lo];
   c.Lq = g.cu_q[lo + 1] - g.cu_q[lo];
   c.kv0 = g.cu_kv[lo];
