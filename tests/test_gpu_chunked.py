@@ -12,6 +12,8 @@ queries at positions L_kv - L_q .. L_kv - 1, the index rebuilt for the chunk
 - The last 8K chunk of the 128K layer prompt, and a paged (64-token pages,
   NaN-poisoned pool) varlen mix: sampled segments.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -147,8 +149,13 @@ def test_chunk_of_128k_sampled(w):
     assert run.device_error() == 0
 
 
-def test_chunk_mix_paged():
-    w = configs.CHUNK_MIX
+@pytest.mark.parametrize("dtype", ["bf16", "e4m3"])
+def test_chunk_mix_paged(dtype):
+    """The paged chunk mix (64-token pages; chunks of 8192 queries over 20000
+    and 65613 keys, a whole 9001-token prompt, a single query, a request with
+    keys only), in bf16 and in E4M3 (per-tensor scales, pooled means on their
+    own scale): sampled segments of every request against the oracle."""
+    w = dataclasses.replace(configs.CHUNK_MIX, name=configs.CHUNK_MIX.name.replace("bf16", dtype), dtype=dtype)
     _note(f"[case] {w.name} lengths={list(w.lengths)} q_lengths={list(w.q_lengths)}")
     b, pg = w.make()
     run = GpuRun(b, paged=pg, alpha=w.alpha, sink=w.sink_blocks, win=w.window_blocks)
@@ -165,6 +172,6 @@ def test_chunk_mix_paged():
         start += ns
     n, amb = compare_csr(P, cu, idx, w.alpha, w.sink_blocks, w.window_blocks, segs=segs)
     _note(f"  CSR: {n} sampled segments, {amb} band differences")
-    out, _ = _attn_check(run, P, segs, cu, idx, "bf16", correction=True)
+    out, _ = _attn_check(run, P, segs, cu, idx, dtype, correction=True)
     _rows_untouched(run, out)
     assert run.device_error() == 0
